@@ -1,0 +1,165 @@
+"""Thin ctypes binding of libthrift.so (the C ABI in include/thrift.h).
+
+Argument marshalling only: torch provides device memory and the current
+stream; every step of the path runs in the library's HIP kernels.  There is
+no fallback: if the library is missing or the tensors are not on a GPU, the
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SO_PATH = os.path.join(HERE, "libthrift.so")
+
+THRIFT_F16, THRIFT_BF16, THRIFT_F32 = 0, 1, 2
+_DT = {torch.float16: THRIFT_F16, torch.bfloat16: THRIFT_BF16, torch.float32: THRIFT_F32}
+
+
+class ThriftError(RuntimeError):
+    pass
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "N", "d", "block", "causal")]
+
+
+_lib = None
+SYMBOLS = ("thrift_quantize", "thrift_select_workspace_bytes", "thrift_list_entries", "thrift_select",
+           "thrift_attn_fwd", "thrift_status_str")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libthrift.so (built in-tree by fp16_long_context_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(SO_PATH):
+            raise ThriftError(f"{SO_PATH} is not built; run `python -m fp16_long_context_amd.build`")
+        L = ctypes.CDLL(SO_PATH)
+        P, i32, f32, f64, sz, i64 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t,
+                                     ctypes.c_int64)
+        SP = ctypes.POINTER(Shape)
+        L.thrift_quantize.argtypes = [SP, i32] + [P] * 12 + [P]
+        L.thrift_quantize.restype = i32
+        L.thrift_select_workspace_bytes.argtypes = [SP]
+        L.thrift_select_workspace_bytes.restype = sz
+        L.thrift_list_entries.argtypes = [SP]
+        L.thrift_list_entries.restype = i64
+        L.thrift_select.argtypes = [SP, f64, P, P, P, P, P, sz, P]
+        L.thrift_select.restype = i32
+        L.thrift_attn_fwd.argtypes = [SP, f32] + [P] * 11 + [P, i32, P, P]
+        L.thrift_attn_fwd.restype = i32
+        L.thrift_status_str.argtypes = [i32]
+        L.thrift_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(rc: int) -> str:
+    return lib().thrift_status_str(rc).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ThriftError(f"{what}: {status_str(rc)} ({rc})")
+
+
+def make_shape(B, Hq, Hkv, N, d, causal=True, block=64) -> Shape:
+    return Shape(B, Hq, Hkv, N, d, block, int(causal))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ThriftError("tensors must be contiguous and on a GPU")
+
+
+def quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> dict:
+    """FP16 copies and MXFP4 codes of q [B,Hq,N,d], k/v [B,Hkv,N,d] (fp16 or bf16).
+    Layouts as in include/thrift.h (v16/v4/v4s are tile-major)."""
+    _need_gpu(q, k, v)
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ThriftError("q, k, v must share dtype fp16 or bf16")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    nb = N // 64
+    dev = q.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    r = {
+        "q16": torch.empty((B, Hq, N, d), dtype=torch.float16, device=dev),
+        "k16": torch.empty((B, Hkv, N, d), dtype=torch.float16, device=dev),
+        "v16": torch.empty((B, Hkv, nb, d, 64), dtype=torch.float16, device=dev),
+        "q4": torch.empty((B, Hq, N, d // 2), **u8), "q4s": torch.empty((B, Hq, N, d // 32), **u8),
+        "k4": torch.empty((B, Hkv, N, d // 2), **u8), "k4s": torch.empty((B, Hkv, N, d // 32), **u8),
+        "v4": torch.empty((B, Hkv, nb, d, 32), **u8), "v4s": torch.empty((B, Hkv, nb, d, 2), **u8),
+    }
+    s = make_shape(B, Hq, Hkv, N, d)
+    rc = lib().thrift_quantize(ctypes.byref(s), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
+                               *[_ptr(r[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
+                               _stream(dev))
+    _check(rc, "thrift_quantize")
+    return r
+
+
+def list_entries(B, Hq, N, causal=True) -> int:
+    s = make_shape(B, Hq, 1, N, 64, causal)
+    return int(lib().thrift_list_entries(ctypes.byref(s)))
+
+
+def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = True, workspace=None):
+    """Traversal lists: idx (int32, per-row FP16 list then FP4 list) and n16 [B,Hq,nb]."""
+    _need_gpu(q16, k16)
+    B, Hq, N, d = q16.shape
+    Hkv = k16.shape[1]
+    s = make_shape(B, Hq, Hkv, N, d, causal)
+    L = lib()
+    ents = int(L.thrift_list_entries(ctypes.byref(s)))
+    wsb = int(L.thrift_select_workspace_bytes(ctypes.byref(s)))
+    if ents <= 0 or wsb <= 0:
+        raise ThriftError("unsupported shape")
+    idx = torch.empty(ents, dtype=torch.int32, device=q16.device)
+    n16 = torch.empty((B, Hq, N // 64), dtype=torch.int32, device=q16.device)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q16.device)
+    rc = L.thrift_select(ctypes.byref(s), float(frac), _ptr(q16), _ptr(k16), _ptr(idx), _ptr(n16), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(q16.device))
+    _check(rc, "thrift_select")
+    return idx, n16
+
+
+def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True, sm_scale: float = 0.0,
+             out_dtype=torch.float32, want_lse: bool = False, out=None, lse=None):
+    """Fused FP16/MXFP4 attention.  Returns (out [B,Hq,N,d], lse [B,Hq,N] or None)."""
+    q16 = qz["q16"]
+    B, Hq, N, d = q16.shape
+    Hkv = qz["k16"].shape[1]
+    _need_gpu(*qz.values(), idx, n16)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=out_dtype, device=q16.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q16.device)
+    s = make_shape(B, Hq, Hkv, N, d, causal)
+    rc = lib().thrift_attn_fwd(ctypes.byref(s), float(sm_scale),
+                               *[_ptr(qz[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
+                               _ptr(idx), _ptr(n16), _ptr(out), _DT[out.dtype], _ptr(lse), _stream(q16.device))
+    _check(rc, "thrift_attn_fwd")
+    return out, lse
+
+
+def attention(q, k, v, frac: float = 0.05, causal: bool = True, sm_scale: float = 0.0, out_dtype=torch.float32):
+    """quantize -> select -> fused attention on the current stream."""
+    qz = quantize(q, k, v)
+    idx, n16 = select(qz["q16"], qz["k16"], frac, causal)
+    out, _ = attn_fwd(qz, idx, n16, causal, sm_scale, out_dtype)
+    return out

@@ -1,0 +1,120 @@
+// C ABI of libthrift (declared in include/thrift.h): argument validation on
+// the host, then launches on the caller's stream.  Validation runs before
+// any HIP call, so an invalid call returns without touching the device.
+#include <math.h>
+
+#include "../../include/thrift.h"
+#include "thrift_internal.h"
+
+using namespace thrift;
+
+namespace {
+
+int check_shape(const thrift_shape *s) {
+  if (!s) return THRIFT_EINVAL;
+  if (s->B <= 0 || s->Hq <= 0 || s->Hkv <= 0 || s->N <= 0 || s->d <= 0 || s->block <= 0) return THRIFT_EINVAL;
+  if (s->Hq % s->Hkv != 0) return THRIFT_EINVAL;
+  if (s->causal != 0 && s->causal != 1) return THRIFT_EINVAL;
+  if (s->d != 64 && s->d != 128) return THRIFT_EUNSUPPORTED;
+  if (s->block != 64) return THRIFT_EUNSUPPORTED;
+  if (s->N % 64 != 0 || s->N / 64 > kMaxBlocks) return THRIFT_EUNSUPPORTED;
+  // grid sizes fit 32 bits
+  const int64_t rows = (int64_t)s->B * s->Hq * (s->N / 64);
+  if (rows > 0x7fffffffLL) return THRIFT_EUNSUPPORTED;
+  return THRIFT_OK;
+}
+
+bool aligned_ok(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *thrift_status_str(int status) {
+  switch (status) {
+    case THRIFT_OK: return "ok";
+    case THRIFT_EINVAL: return "invalid argument";
+    case THRIFT_EUNSUPPORTED: return "unsupported shape";
+    case THRIFT_EWORKSPACE: return "workspace missing or too small";
+    case THRIFT_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t thrift_select_workspace_bytes(const thrift_shape *s) {
+  if (check_shape(s) != THRIFT_OK) return 0;
+  return (size_t)4 * (size_t)(s->N / 64) * (size_t)s->d * (size_t)s->B * (size_t)(s->Hq + s->Hkv);
+}
+
+int64_t thrift_list_entries(const thrift_shape *s) {
+  if (check_shape(s) != THRIFT_OK) return 0;
+  const int64_t nb = s->N / 64;
+  return (int64_t)s->B * s->Hq * (s->causal ? nb * (nb + 1) / 2 : nb * nb);
+}
+
+int thrift_quantize(const thrift_shape *s, int in_dtype, const void *q, const void *k, const void *v, void *q16,
+                    void *k16, void *v16, void *q4, void *q4s, void *k4, void *k4s, void *v4, void *v4s,
+                    void *stream) {
+  int rc = check_shape(s);
+  if (rc != THRIFT_OK) return rc;
+  if (in_dtype != THRIFT_F16 && in_dtype != THRIFT_BF16) return THRIFT_EINVAL;
+  const void *ptrs[] = {q, k, v, q16, k16, v16, q4, q4s, k4, k4s, v4, v4s};
+  for (const void *p : ptrs)
+    if (!aligned_ok(p)) return THRIFT_EINVAL;
+  QuantArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.q16 = (uint16_t *)q16; a.k16 = (uint16_t *)k16; a.v16 = (uint16_t *)v16;
+  a.q4 = (uint8_t *)q4; a.q4s = (uint8_t *)q4s; a.k4 = (uint8_t *)k4; a.k4s = (uint8_t *)k4s;
+  a.v4 = (uint8_t *)v4; a.v4s = (uint8_t *)v4s;
+  a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d;
+  a.bf16 = in_dtype == THRIFT_BF16;
+  return launch_quantize(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
+int thrift_select(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx, int32_t *n16,
+                  void *workspace, size_t ws_bytes, void *stream) {
+  int rc = check_shape(s);
+  if (rc != THRIFT_OK) return rc;
+  if (!(frac >= 0.0 && frac <= 1.0)) return THRIFT_EINVAL;  // also rejects NaN
+  const void *ptrs[] = {q16, k16, idx, n16};
+  for (const void *p : ptrs)
+    if (!aligned_ok(p)) return THRIFT_EINVAL;
+  const size_t need = thrift_select_workspace_bytes(s);
+  if (!workspace || ws_bytes < need) return THRIFT_EWORKSPACE;
+  if (!aligned_ok(workspace)) return THRIFT_EINVAL;
+  SelectArgs a;
+  a.q16 = (const uint16_t *)q16; a.k16 = (const uint16_t *)k16;
+  a.idx = idx; a.n16 = n16;
+  a.qbar = (float *)workspace;
+  a.kbarT = (float *)workspace + (size_t)s->B * s->Hq * (s->N / 64) * s->d;
+  a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
+  a.ppm = (int64_t)llround(frac * 1e6);
+  return launch_select(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
+int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
+                    const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
+                    const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype, float *lse,
+                    void *stream) {
+  int rc = check_shape(s);
+  if (rc != THRIFT_OK) return rc;
+  if (out_dtype != THRIFT_F16 && out_dtype != THRIFT_BF16 && out_dtype != THRIFT_F32) return THRIFT_EINVAL;
+  if (!(sm_scale == sm_scale) || isinf(sm_scale)) return THRIFT_EINVAL;
+  const void *ptrs[] = {q16, k16, v16, q4, q4s, k4, k4s, v4, v4s, idx, n16, out};
+  for (const void *p : ptrs)
+    if (!aligned_ok(p)) return THRIFT_EINVAL;
+  if (lse && ((uintptr_t)lse & 15u)) return THRIFT_EINVAL;
+  AttnArgs a;
+  a.q16 = (const uint16_t *)q16; a.k16 = (const uint16_t *)k16; a.v16 = (const uint16_t *)v16;
+  a.q4 = (const uint8_t *)q4; a.q4s = (const uint8_t *)q4s; a.k4 = (const uint8_t *)k4;
+  a.k4s = (const uint8_t *)k4s; a.v4 = (const uint8_t *)v4; a.v4s = (const uint8_t *)v4s;
+  a.idx = idx; a.n16 = n16; a.out = out; a.lse = lse;
+  a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
+  a.out_dtype = out_dtype;
+  // score scale in log2 units, rounded once to fp32
+  const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)s->d));
+  a.c = (float)((double)sm * 1.4426950408889634074);
+  return launch_attn_fwd(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// Step 2 of the ThriftAttention path ("ThriftAttention: Selective Mixed
+// Precision for Long-Context FP4 Attention", abstract: a heuristic rapidly
+// selects a small number of important query-key block pairs for FP16).
+//
+// Heuristic: mean-pool every 64-row block of Q (per query head) and K (per
+// KV head); score the pair (i, j) by the fp64 dot product of the means taken
+// in channel order; per (b, h_q, i) keep the first and diagonal key blocks
+// and the best-scoring others up to ceil(frac * valid blocks) in total.
+//
+// Bit-exactness: the pooled sums of 64 fp16 values are exact in fp64 (they
+// need at most 46 significant bits), so their order does not matter; each
+// product of two fp32 means is exact in fp64, so a sequential fma chain in
+// channel order gives the same bits as any sequential multiply-add in that
+// order.
+#include "thrift_internal.h"
+
+namespace thrift {
+
+// One thread per (head row-block, channel).  Q means are written row-major
+// [BH, nb, d]; K means transposed [BH, d, nb] so that the scoring kernel
+// reads them coalesced.
+template <bool TRANSPOSED>
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t *__restrict__ x16, float *__restrict__ out,
+                                                   int64_t BH, int N, int d) {
+  const int nb = N / 64;
+  const int64_t total = BH * nb * d;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(t % d);
+    const int64_t bi = t / d;  // = bh * nb + i
+    const int64_t bh = bi / nb;
+    const int i = (int)(bi % nb);
+    const uint16_t *p = x16 + (bh * N + 64 * (int64_t)i) * d + c;
+    double s = 0.0;
+#pragma unroll 8
+    for (int r = 0; r < 64; r++) s += (double)__builtin_bit_cast(_Float16, p[(int64_t)r * d]);
+    const float m = (float)(s * (1.0 / 64.0));
+    if (TRANSPOSED)
+      out[(bh * d + c) * nb + i] = m;
+    else
+      out[bi * d + c] = m;
+  }
+}
+
+// Order-preserving map of a double to uint64 (larger value -> larger key);
+// -0 is folded onto +0 so that equal scores compare equal.
+__device__ __forceinline__ uint64_t order_key(double s) {
+  if (s == 0.0) s = 0.0;
+  uint64_t u = __double_as_longlong(s);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+constexpr int kSelThreads = 256;
+
+// Exclusive prefix sum of one value per thread over the block; also returns
+// the total.  `buf` holds kSelThreads ints.
+__device__ int block_exclusive_scan(int v, int *buf, int &total) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    int add = (t >= off) ? buf[t - off] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  total = buf[kSelThreads - 1];
+  int r = buf[t] - v;
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per (b, h_q, query block i).
+__global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a) {
+  extern __shared__ uint64_t keys[];  // [n_valid]
+  __shared__ double qrow[128];
+  __shared__ int hist[256];
+  __shared__ int scan_buf[kSelThreads];
+  __shared__ int s_digit, s_above;
+
+  const int nb = a.N / 64;
+  const int64_t row = blockIdx.x;  // = (b*Hq + h)*nb + i
+  const int i = (int)(row % nb);
+  const int64_t bh = row / nb;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int g = (int)((int64_t)h * a.Hkv / a.Hq);
+  const int nv = a.causal ? i + 1 : nb;
+  const int tid = threadIdx.x;
+  const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
+  int32_t *out = a.idx + bh * per + (a.causal ? (int64_t)i * (i + 1) / 2 : (int64_t)i * nb);
+
+  if (a.ppm == 0) {  // no FP16 blocks: the FP4 list is every valid block
+    for (int j = tid; j < nv; j += kSelThreads) out[j] = j;
+    if (tid == 0) a.n16[row] = 0;
+    return;
+  }
+  const int nforced = (i == 0) ? 1 : 2;
+  int64_t want = (a.ppm * nv + 999999) / 1000000;
+  int64_t kk = want > nforced ? want : nforced;
+  if (kk > nv) kk = nv;
+  const int kextra = (int)kk - nforced;  // best non-forced blocks to add
+
+  // contiguous chunk of block indices per thread (keeps index order for scans)
+  const int chunk = (nv + kSelThreads - 1) / kSelThreads;
+  const int j0 = tid * chunk, j1 = min(nv, j0 + chunk);
+
+  if (kextra > 0 && kextra < nv - nforced) {
+    for (int c = tid; c < a.d; c += kSelThreads) qrow[c] = (double)a.qbar[row * a.d + c];
+    __syncthreads();
+    // scores: strided j for coalesced reads of the transposed K means
+    const float *kT = a.kbarT + (int64_t)(b * a.Hkv + g) * a.d * nb;
+    for (int j = tid; j < nv; j += kSelThreads) {
+      double s = 0.0;
+      for (int c = 0; c < a.d; c++) s = fma(qrow[c], (double)kT[(int64_t)c * nb + j], s);
+      keys[j] = order_key(s);
+    }
+    __syncthreads();
+    // radix select (8 bits per pass, most significant first) of the kextra-th
+    // largest key among the non-forced blocks
+    uint64_t prefix = 0, pmask = 0;
+    int remaining = kextra;
+    for (int pass = 0; pass < 8; pass++) {
+      const int shift = 56 - 8 * pass;
+      hist[tid] = 0;  // kSelThreads == 256 bins
+      __syncthreads();
+      for (int j = tid; j < nv; j += kSelThreads) {
+        if (j == 0 || j == i) continue;
+        const uint64_t kj = keys[j];
+        if ((kj & pmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int above = 0, dgt = 255;
+        for (; dgt > 0; dgt--) {
+          if (above + hist[dgt] >= remaining) break;
+          above += hist[dgt];
+        }
+        s_digit = dgt;
+        s_above = above;
+      }
+      __syncthreads();
+      remaining -= s_above;
+      prefix |= (uint64_t)s_digit << shift;
+      pmask |= (uint64_t)255 << shift;
+      __syncthreads();
+    }
+    // prefix is the threshold key T: take every key > T and the `remaining`
+    // lowest-index keys == T
+    int neq = 0;
+    for (int j = j0; j < j1; j++)
+      if (j != 0 && j != i && keys[j] == prefix) neq++;
+    int tot;
+    int rank = block_exclusive_scan(neq, scan_buf, tot);
+    // mark the FP16 set in the key array: 1 = FP16, 0 = FP4
+    for (int j = j0; j < j1; j++) {
+      uint64_t kj = keys[j];
+      int sel;
+      if (j == 0 || j == i)
+        sel = 1;
+      else if (kj > prefix)
+        sel = 1;
+      else if (kj == prefix)
+        sel = (rank++ < remaining);
+      else
+        sel = 0;
+      keys[j] = (uint64_t)sel;  // only this thread touches its chunk from here
+    }
+    __syncthreads();
+  } else {
+    // all non-forced blocks (kextra == nv - nforced) or none (kextra == 0)
+    const uint64_t v = kextra > 0 ? 1 : 0;
+    for (int j = j0; j < j1; j++) keys[j] = (j == 0 || j == i) ? 1 : v;
+    __syncthreads();
+  }
+  // emit: FP16 list ascending, then FP4 list ascending
+  int c16 = 0;
+  for (int j = j0; j < j1; j++) c16 += (int)keys[j];
+  int tot16;
+  int p16 = block_exclusive_scan(c16, scan_buf, tot16);
+  int p4 = tot16 + (j0 - p16);  // FP4 entries before this chunk = blocks before it minus FP16 ones
+  for (int j = j0; j < j1; j++) {
+    if (keys[j])
+      out[p16++] = j;
+    else
+      out[p4++] = j;
+  }
+  if (tid == 0) a.n16[row] = tot16;
+}
+
+hipError_t launch_select(const SelectArgs &a, hipStream_t st) {
+  const int nb = a.N / 64;
+  auto grid = [](int64_t work) {
+    int64_t b = (work + 255) / 256;
+    return (unsigned)(b > 256 * 64 ? 256 * 64 : b);
+  };
+  const int64_t BHq = (int64_t)a.B * a.Hq, BHk = (int64_t)a.B * a.Hkv;
+  hipLaunchKernelGGL(pool_kernel<false>, dim3(grid(BHq * nb * a.d)), dim3(256), 0, st, a.q16, a.qbar, BHq, a.N, a.d);
+  hipLaunchKernelGGL(pool_kernel<true>, dim3(grid(BHk * nb * a.d)), dim3(256), 0, st, a.k16, a.kbarT, BHk, a.N, a.d);
+  const size_t lds = sizeof(uint64_t) * (size_t)nb;
+  hipError_t e = hipFuncSetAttribute((const void *)score_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(score_select_kernel, dim3((unsigned)(BHq * nb)), dim3(kSelThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace thrift

@@ -1,0 +1,71 @@
+// Internal declarations shared by the HIP sources of libthrift (not part of
+// the C ABI).  Device helpers for the gfx950 MXFP4 and MFMA paths.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace thrift {
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+// Largest supported number of 64-row blocks (bounds the LDS the selection
+// and attention kernels reserve per block row).
+constexpr int kMaxBlocks = 8192;
+
+// E8M0 scale byte of an MXFP4 group from the bit pattern of its largest
+// magnitude (a normal or zero fp32): floor(log2 amax) - 2 + 127, clamped at
+// 0 (amax = 0 or amax < 2^-124).
+__device__ __forceinline__ int mx_scale_byte(float amax) {
+  int biased = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  int s = biased - 2;
+  return s > 0 ? s : 0;
+}
+
+// The power of two the hardware convert divides by for scale byte s (s >= 1);
+// byte 0 only occurs for groups whose values are all zero or below 2^-124,
+// which convert to zero codes under a divisor of 1.
+__device__ __forceinline__ float mx_scale_divisor(int s) { return s > 0 ? __uint_as_float((uint32_t)s << 23) : 1.0f; }
+
+// Two fp32 values divided by `div` and rounded to E2M1 (nearest-even,
+// saturating, sign kept) into byte `sel` of `word`: low nibble = a.
+// v_cvt_scalef32_pk_fp4_f32 on gfx950 computes exactly this.
+#define THRIFT_CVT_FP4(word, a, b, div, sel) \
+  (word) = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((word), (a), (b), (div), (sel))
+
+struct QuantArgs {
+  const void *q, *k, *v;
+  uint16_t *q16, *k16, *v16;
+  uint8_t *q4, *q4s, *k4, *k4s, *v4, *v4s;
+  int B, Hq, Hkv, N, d;
+  int bf16;
+};
+
+struct SelectArgs {
+  const uint16_t *q16, *k16;
+  int32_t *idx, *n16;
+  float *qbar;   // [B,Hq,nb,d]
+  float *kbarT;  // [B,Hkv,d,nb]
+  int B, Hq, Hkv, N, d, causal;
+  int64_t ppm;
+};
+
+struct AttnArgs {
+  const uint16_t *q16, *k16, *v16;
+  const uint8_t *q4, *q4s, *k4, *k4s, *v4, *v4s;
+  const int32_t *idx, *n16;
+  void *out;
+  float *lse;
+  int B, Hq, Hkv, N, d, causal, out_dtype;
+  float c;  // fl32(sm_scale * log2 e)
+};
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
+hipError_t launch_select(const SelectArgs &a, hipStream_t st);
+hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st);
+
+}  // namespace thrift

@@ -1,0 +1,151 @@
+/*
+ * thrift.h -- C ABI of the MI355X (gfx950) ThriftAttention prefill library.
+ *
+ * The method ("ThriftAttention: Selective Mixed Precision for Long-Context
+ * FP4 Attention", abstract): a heuristic first picks a small number of
+ * important query-key block pairs for FP16; the picked blocks are then
+ * computed in FP16 and all other causally valid blocks in block-scaled
+ * 4-bit, and both paths are merged by online softmax into one output.  The
+ * three calls below are the three steps of that path:
+ *
+ *   thrift_quantize   FP16 copies of Q/K/V and their MXFP4 codes
+ *   thrift_select     the block heuristic: FP16 and FP4 traversal lists
+ *   thrift_attn_fwd   fused mixed-precision attention with one online softmax
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers owned and allocated by the caller;
+ *     the library allocates nothing, keeps no state between calls and never
+ *     synchronizes.  All work is enqueued on `stream` (a hipStream_t; NULL =
+ *     the default stream) and is asynchronous; calls are reentrant.
+ *   - Every pointer must be 16-byte aligned.
+ *   - Return value: THRIFT_OK (0) or a negative thrift_status.  Arguments are
+ *     validated on the host before anything is enqueued, so an error return
+ *     other than THRIFT_EHIP means nothing was launched.  THRIFT_EHIP reports
+ *     a HIP launch error (hipGetLastError after the launch).
+ *   - Shapes: B, Hq, Hkv, N > 0; Hq % Hkv == 0 (query head h reads KV head
+ *     floor(h * Hkv / Hq)); d in {64, 128}; block == 64; N % 64 == 0;
+ *     causal in {0, 1}; otherwise THRIFT_EINVAL (bad values) or
+ *     THRIFT_EUNSUPPORTED (valid but not built: other d, block, N % 64 != 0).
+ *   - Inputs must be finite with |x| <= 65504; other values give undefined
+ *     output but no out-of-bounds access.
+ *   - nb = N / 64 blocks.  MXFP4 = OCP MX: E2M1 codes (sign bit 3, element
+ *     2j of a group in the low nibble of byte j) with one E8M0 scale byte per
+ *     32 elements; scale exponent = floor(log2 amax) - 2 (byte 0 for an
+ *     all-zero group), elements rounded to nearest-even on the E2M1 grid and
+ *     saturated to +-6.
+ */
+#ifndef THRIFT_H
+#define THRIFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  THRIFT_OK = 0,
+  THRIFT_EINVAL = -1,      /* null/misaligned pointer, bad value */
+  THRIFT_EUNSUPPORTED = -2,/* a shape this build does not handle */
+  THRIFT_EWORKSPACE = -3,  /* workspace missing or too small */
+  THRIFT_EHIP = -4         /* HIP launch error */
+} thrift_status;
+
+typedef enum { THRIFT_F16 = 0, THRIFT_BF16 = 1, THRIFT_F32 = 2 } thrift_dtype;
+
+/* Problem statement: batch, query heads, KV heads, tokens, head dim, block
+ * size (must be 64), causal mask flag. */
+typedef struct {
+  int32_t B, Hq, Hkv, N, d, block, causal;
+} thrift_shape;
+
+/*
+ * Step 1 -- quantize (the block-scaled 4-bit operands of the FP4 path and the
+ * FP16 operands of the FP16 path; the abstract's "block-scaled quantisation").
+ *
+ * in_dtype: THRIFT_F16 or THRIFT_BF16 for q, k, v.
+ * Inputs (row-major): q [B,Hq,N,d], k and v [B,Hkv,N,d].
+ * Outputs (all written completely):
+ *   q16 [B,Hq,N,d], k16 [B,Hkv,N,d]   fp16, nearest-even rounding of the input
+ *   v16 [B,Hkv,nb,d,64]               fp16, per 64-token block channel-major
+ *                                     (element (t, c) at [t/64][c][t%64])
+ *   q4 [B,Hq,N,d/2], q4s [B,Hq,N,d/32]     MXFP4 of q16, groups of 32 channels
+ *   k4 [B,Hkv,N,d/2], k4s [B,Hkv,N,d/32]   MXFP4 of k16, groups of 32 channels
+ *   v4 [B,Hkv,nb,d,32], v4s [B,Hkv,nb,d,2] MXFP4 of v16, groups of 32 tokens of
+ *                                     one channel (token 64n + 32g + e is
+ *                                     element e of group g of block n)
+ * Errors: THRIFT_EINVAL for a null or misaligned pointer or a bad dtype.
+ */
+int thrift_quantize(const thrift_shape *s, int in_dtype, const void *q, const void *k, const void *v,
+                    void *q16, void *k16, void *v16, void *q4, void *q4s, void *k4, void *k4s, void *v4,
+                    void *v4s, void *stream);
+
+/* Bytes of device workspace thrift_select needs (pooled fp32 means of Q and
+ * K): 4 * nb * d * B * (Hq + Hkv).  Returns 0 for an invalid shape. */
+size_t thrift_select_workspace_bytes(const thrift_shape *s);
+
+/* int32 entries of the traversal-list array: B * Hq * nb(nb+1)/2 (causal) or
+ * B * Hq * nb * nb.  Returns 0 for an invalid shape. */
+int64_t thrift_list_entries(const thrift_shape *s);
+
+/*
+ * Step 2 -- select (the abstract's "heuristic rapidly selects a small number
+ * of important query-key block pairs for FP16").
+ *
+ * Heuristic: each 64-row block of q16 (per query head) and k16 (per KV head)
+ * is mean-pooled (exact sum, one rounding to fp32); a block pair (i, j) is
+ * scored by the fp64 dot product of the two means, accumulated in channel
+ * order.  Per (b, h_q, query block i), with n_valid = i + 1 (causal) or nb,
+ * ppm = llround(frac * 1e6) and forced blocks F = {0, i}:
+ *   ppm == 0:  no FP16 blocks;
+ *   else:      budget k = min(n_valid, max(|F|, ceil(ppm * n_valid / 1e6)));
+ *              FP16 list = F plus the k - |F| best other blocks by
+ *              (score descending, block index ascending).
+ * The FP4 list is every other valid block.
+ *
+ * frac in [0, 1].  Outputs:
+ *   idx [B,Hq, rows]: row i starts at i(i+1)/2 (causal) or i*nb and holds the
+ *        FP16 list ascending followed by the FP4 list ascending;
+ *   n16 [B,Hq,nb]: length of each FP16 list.
+ * workspace: device buffer of at least thrift_select_workspace_bytes(s)
+ * bytes (contents on return: the pooled means, Q first then K).
+ * Errors: THRIFT_EINVAL (pointer, frac), THRIFT_EWORKSPACE.
+ */
+int thrift_select(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx,
+                  int32_t *n16, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Step 3 -- fused mixed-precision attention (the abstract's "selected blocks
+ * are computed in FP16 and the remaining blocks in FP4, with both paths
+ * merged via online softmax into a single output").
+ *
+ * For query row t of (b, h) in block i, every valid key (causal: key <= t)
+ * of a block on the row's FP16 list is scored in FP16 (fp32 accumulation)
+ * and every key of a block on its FP4 list from the MXFP4 codes.  With
+ * c = fl32(sm_scale * log2(e)) (sm_scale <= 0 means 1/sqrt(d)), x = score * c,
+ * an integer running max M = ceil(max x) and p = 2^(x - M):
+ *   l   = sum of p over all valid keys;
+ *   FP16 blocks add fp16(p) * v16 to the accumulator;
+ *   FP4 blocks re-quantize p to MXFP4 per aligned 32-key group and add the
+ *   MXFP4 product with v4;
+ *   out = acc / l;  lse = (M + log2 l) * ln 2 (natural-log LSE of the scaled
+ *   scores).
+ * out [B,Hq,N,d] of out_dtype (THRIFT_F32, THRIFT_F16 or THRIFT_BF16);
+ * lse [B,Hq,N] fp32, may be NULL.  idx/n16 must come from thrift_select with
+ * the same shape (entries outside [0, n_valid) are not checked).
+ * Errors: THRIFT_EINVAL (pointer, dtype).
+ */
+int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
+                    const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
+                    const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
+                    float *lse, void *stream);
+
+/* Static string naming a status code. */
+const char *thrift_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* THRIFT_H */
