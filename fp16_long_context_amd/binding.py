@@ -85,25 +85,32 @@ def _need_gpu(*ts):
             raise ThriftError("tensors must be contiguous and on a GPU")
 
 
-def quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> dict:
+def alloc_quantized(B, Hq, Hkv, N, d, device) -> dict:
+    """Output buffers of quantize (layouts as in include/thrift.h)."""
+    nb = N // 64
+    u8 = dict(dtype=torch.uint8, device=device)
+    return {
+        "q16": torch.empty((B, Hq, N, d), dtype=torch.float16, device=device),
+        "k16": torch.empty((B, Hkv, N, d), dtype=torch.float16, device=device),
+        "v16": torch.empty((B, Hkv, nb, d, 64), dtype=torch.float16, device=device),
+        "q4": torch.empty((B, Hq, N, d // 2), **u8), "q4s": torch.empty((B, Hq, N, d // 32), **u8),
+        "k4": torch.empty((B, Hkv, N, d // 2), **u8), "k4s": torch.empty((B, Hkv, N, d // 32), **u8),
+        "v4": torch.empty((B, Hkv, nb, d, 32), **u8), "v4s": torch.empty((B, Hkv, nb, d, 2), **u8),
+    }
+
+
+def quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: dict | None = None) -> dict:
     """FP16 copies and MXFP4 codes of q [B,Hq,N,d], k/v [B,Hkv,N,d] (fp16 or bf16).
-    Layouts as in include/thrift.h (v16/v4/v4s are tile-major)."""
+    Layouts as in include/thrift.h (v16/v4/v4s are tile-major).  `out` may
+    hold preallocated buffers from alloc_quantized."""
     _need_gpu(q, k, v)
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
         raise ThriftError("q, k, v must share dtype fp16 or bf16")
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
-    nb = N // 64
     dev = q.device
-    u8 = dict(dtype=torch.uint8, device=dev)
-    r = {
-        "q16": torch.empty((B, Hq, N, d), dtype=torch.float16, device=dev),
-        "k16": torch.empty((B, Hkv, N, d), dtype=torch.float16, device=dev),
-        "v16": torch.empty((B, Hkv, nb, d, 64), dtype=torch.float16, device=dev),
-        "q4": torch.empty((B, Hq, N, d // 2), **u8), "q4s": torch.empty((B, Hq, N, d // 32), **u8),
-        "k4": torch.empty((B, Hkv, N, d // 2), **u8), "k4s": torch.empty((B, Hkv, N, d // 32), **u8),
-        "v4": torch.empty((B, Hkv, nb, d, 32), **u8), "v4s": torch.empty((B, Hkv, nb, d, 2), **u8),
-    }
+    r = alloc_quantized(B, Hq, Hkv, N, d, dev) if out is None else out
+    _need_gpu(*r.values())
     s = make_shape(B, Hq, Hkv, N, d)
     rc = lib().thrift_quantize(ctypes.byref(s), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
                                *[_ptr(r[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
@@ -117,8 +124,10 @@ def list_entries(B, Hq, N, causal=True) -> int:
     return int(lib().thrift_list_entries(ctypes.byref(s)))
 
 
-def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = True, workspace=None):
-    """Traversal lists: idx (int32, per-row FP16 list then FP4 list) and n16 [B,Hq,nb]."""
+def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = True, workspace=None, idx=None,
+           n16=None):
+    """Traversal lists: idx (int32, per-row FP16 list then FP4 list) and n16 [B,Hq,nb].
+    idx, n16 and the workspace may be preallocated."""
     _need_gpu(q16, k16)
     B, Hq, N, d = q16.shape
     Hkv = k16.shape[1]
@@ -128,8 +137,12 @@ def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = Tru
     wsb = int(L.thrift_select_workspace_bytes(ctypes.byref(s)))
     if ents <= 0 or wsb <= 0:
         raise ThriftError("unsupported shape")
-    idx = torch.empty(ents, dtype=torch.int32, device=q16.device)
-    n16 = torch.empty((B, Hq, N // 64), dtype=torch.int32, device=q16.device)
+    if idx is None:
+        idx = torch.empty(ents, dtype=torch.int32, device=q16.device)
+    if n16 is None:
+        n16 = torch.empty((B, Hq, N // 64), dtype=torch.int32, device=q16.device)
+    if idx.numel() < ents or n16.numel() < B * Hq * (N // 64) or idx.dtype != torch.int32 or n16.dtype != torch.int32:
+        raise ThriftError("idx/n16 buffers too small or not int32")
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q16.device)
     rc = L.thrift_select(ctypes.byref(s), float(frac), _ptr(q16), _ptr(k16), _ptr(idx), _ptr(n16), _ptr(workspace),
@@ -147,6 +160,8 @@ def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True
     _need_gpu(*qz.values(), idx, n16)
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=out_dtype, device=q16.device)
+    if out.shape != (B, Hq, N, d) or out.dtype not in _DT:
+        raise ThriftError("out must be [B,Hq,N,d] fp32/fp16/bf16")
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q16.device)
     s = make_shape(B, Hq, Hkv, N, d, causal)

@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(_SO)
         P = ctypes.c_void_p
         i32, i64, f32, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = i32
         L.oracle_to_fp16.argtypes = [P, i32, P, i64]
         L.oracle_to_fp16.restype = None
         L.oracle_mx_encode.argtypes = [P, i64, P, P]
@@ -66,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_attn_rows.restype = i32
         _lib = L
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oracle_threads())
 
 
 def _p(a):

@@ -41,6 +41,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 #define ORC_OK 0
 #define ORC_EINVAL -1
 
@@ -141,6 +145,15 @@ static double e8m0_value(uint8_t s) { return ldexp(1.0, (int)s - 127); }
 
 /* packed nibble accessors: element 2j in the low nibble of byte j */
 static int nib(const uint8_t *p, int64_t i) { return (p[i >> 1] >> ((i & 1) * 4)) & 15; }
+
+/* Threads an OpenMP region of the oracle uses (1 without OpenMP). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------ */
 /* Exported scalar helpers (used by the oracle's own pin tests)         */
