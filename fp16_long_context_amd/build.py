@@ -22,6 +22,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-ta
          "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
 
 
+# The fused kernel never produces or consumes NaNs (inputs are finite by
+# contract; masked scores are -inf), so fmax needs no NaN canonicalisation.
+PER_FILE = {"attn_fwd.hip": ["-fno-honor-nans"]}
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if c and (os.path.isabs(c) and os.path.exists(c) or not os.path.isabs(c)):
@@ -37,7 +42,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *FLAGS, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         # the host pass does not know the gfx950 target feature: harmless
         err = "\n".join(x for x in r.stderr.splitlines() if "packed-fp32-ops" not in x)

@@ -36,8 +36,12 @@
 namespace thrift {
 
 constexpr float kLazy = 8.0f;
+// Largest power-of-two shift an FP4-only tile may fold into P's scale.  With
+// |v| <= 2^16, at most 2^19 keys and p <= 2^kLazy, acc stays below
+// 2^(64 + 8 + 16 + 19) = 2^107 and P's scale byte below 133 + 64 = 197.
+constexpr float kMaxShift = 64.0f;
 
-template <int D>
+template <int D, int HPW>
 struct Tile {
   // FP4 stage
   static constexpr int K4 = 64 * D / 2, K4S = 64 * D / 32, V4 = D * 32, V4S = D * 2;
@@ -46,10 +50,40 @@ struct Tile {
   static constexpr int K16 = 64 * D * 2, V16 = D * 64 * 2;
   static constexpr int FP16_BYTES = K16 + V16;
   static constexpr int STAGE = FP4_BYTES + FP16_BYTES;
-  // offsets inside a stage
-  static constexpr int oK4 = 0, oK4S = K4, oV4 = K4 + K4S, oV4S = K4 + K4S + V4;
+  // offsets inside a stage: codes first (whole 1 KB groups per region), then
+  // the K and V scale bytes
+  static constexpr int oK4 = 0, oV4 = K4, oK4S = K4 + V4, oV4S = K4 + V4 + K4S;
+  static constexpr int G4 = (K4 + V4) / 1024;    // 64-chunk groups of FP4 codes
+  static constexpr int SC4 = (K4S + V4S) / 16;   // 16-byte chunks of FP4 scales
+  static constexpr int G16 = (K16 + V16) / 1024; // 64-chunk groups of the FP16 stage
+  // the FP4-only walk uses a 3-slot ring of FP4 stages in the same memory
+  static constexpr int RING = FP4_BYTES;
   static constexpr int oK16 = FP4_BYTES, oV16 = FP4_BYTES + K16;
+  // after the two stages: the workgroup's Q16 rows ([HPW*64][D] halves,
+  // 16-byte chunks XOR-swizzled by row) and the FP16-list bitmasks
+  static constexpr int oQ16 = 2 * STAGE;
+  static constexpr int Q16_BYTES = HPW * 64 * D * 2;
+  static constexpr int oMASK = oQ16 + Q16_BYTES;
+  static constexpr int oUMASK = oMASK + HPW * (kMaxBlocks / 32) * 4;  // union of the heads' FP16 lists
+  static constexpr int LDS = oUMASK + (kMaxBlocks / 32) * 4;
 };
+
+// LDS layouts of the staged tiles are XOR-swizzled in 16-byte chunks so that
+// the MFMA operand reads (32 permuted key rows, or 32 consecutive channel
+// rows, at the same logical chunk) spread over all LDS banks.  Physical chunk
+// = logical chunk ^ swz(row).  The loader applies the same map to the source
+// address, so the direct global->LDS copy stays a plain per-lane transfer.
+template <int D>
+__device__ __forceinline__ int swz_k4(int key) {  // K4 rows: D/32 chunks
+  if (D == 128) return ((key >> 2) & 1) | (((key >> 5) & 1) << 1);
+  return (key >> 5) & 1;
+}
+template <int D>
+__device__ __forceinline__ int swz_k16(int key) {  // K16 rows: D/8 chunks
+  if (D == 128) return (key & 3) | (((key >> 2) & 1) << 2) | (((key >> 5) & 1) << 3);
+  return ((key >> 1) & 1) | (((key >> 2) & 1) << 1) | (((key >> 5) & 1) << 2);
+}
+__device__ __forceinline__ int swz_v16(int ch) { return (ch >> 1) & 7; }  // V16 rows: 8 chunks
 
 // Key (row of the 64-key tile) that A-operand row rho of MFMA block blk
 // reads, so that the result lands in the lane layout described above.
@@ -57,20 +91,272 @@ __device__ __forceinline__ int permuted_key(int rho, int blk) {
   return 32 * ((rho >> 2) & 1) + 16 * blk + 4 * (rho >> 3) + (rho & 3);
 }
 
+// 16 bytes per lane from global memory straight into LDS at lds_wave_base +
+// 16 * lane (lds_wave_base must be the same for the whole wave).
+__device__ __forceinline__ void load_to_lds(const void *g, uint8_t *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including the
+// direct-to-LDS ones) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The value x of lane l^32 (v_permlane32_swap exchanges the wave's halves).
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Largest of this lane's 32 scores (v_max3 chain).
+__device__ __forceinline__ float lane_max32(const float16v (&s)[2]) {
+  float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) {
+    m0 = fmaxf(fmaxf(m0, s[0][r]), s[0][r + 1]);
+    m1 = fmaxf(fmaxf(m1, s[1][r]), s[1][r + 1]);
+  }
+  return fmaxf(m0, m1);
+}
+
+// Online-softmax step on one 32-query x 64-key score tile held as s[2]
+// (this lane: query col, keys 32*lh + 0..31).  Applies the causal mask on
+// the diagonal tile, raises the integer running max when needed (rescaling
+// acc and the row sum by an exact power of two), replaces s by
+// p = 2^(s*c - M) and adds the lane's p to l_part.  Returns the lane's
+// largest raw score (-inf if all masked).
+template <int CB, bool MASK>
+__device__ __forceinline__ float softmax_step(float16v (&s)[2], float16v (&acc)[CB], float &M, float &l_part,
+                                              float &mt_max, const float c, const int lh, const int qpos) {
+  if (MASK) {
+#pragma unroll
+    for (int blk = 0; blk < 2; blk++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        if (32 * lh + 16 * blk + r > qpos) s[blk][r] = -INFINITY;
+  }
+  const float lane_max = lane_max32(s);
+  const float row_max = fmaxf(lane_max, other_half(lane_max));
+  const float mt = ceilf(row_max * c);  // integer candidate max (log2 units)
+  mt_max = fmaxf(mt_max, mt);
+  const bool raise = (mt > M + kLazy) || (M == -INFINITY);
+  if (__ballot(raise)) {  // wave-uniform; lanes that keep their max scale by 1
+    const float sc = raise ? ((M == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(M - mt))) : 1.0f;
+    M = raise ? mt : M;
+    l_part *= sc;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[cb][r] *= sc;
+  }
+  const float negM = -M;
+  float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    s[0][r] = __builtin_amdgcn_exp2f(fmaf(s[0][r], c, negM));
+    s[1][r] = __builtin_amdgcn_exp2f(fmaf(s[1][r], c, negM));
+    l0 += s[0][r];
+    l1 += s[1][r];
+  }
+  l_part += l0 + l1;
+  return lane_max;
+}
+
+// S^T = K4 Q4^T of an FP4 tile for the two 32-key halves of the permuted tile.
+template <int D, int HPW>
+__device__ __forceinline__ void fp4_qk(const uint8_t *st, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
+                                       const int col, const int lh, float16v (&s)[2]) {
+  using T = Tile<D, HPW>;
+  constexpr int KS = D / 64;
+  int4v ka[2][KS];
+  int ks[2][KS];
+#pragma unroll
+  for (int blk = 0; blk < 2; blk++) {
+    const int key = permuted_key(col, blk);
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) {
+      ka[blk][kk] = *(const int4v *)(st + T::oK4 + key * (D / 2) + 16 * ((2 * kk + lh) ^ swz_k4<D>(key)));
+      ks[blk][kk] = st[T::oK4S + key * (D / 32) + 2 * kk + lh];
+    }
+  }
+#pragma unroll
+  for (int blk = 0; blk < 2; blk++) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) s[blk][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KS; kk++) {
+      int8v a8 = {ka[blk][kk][0], ka[blk][kk][1], ka[blk][kk][2], ka[blk][kk][3], 0, 0, 0, 0};
+      int8v b8 = {qf4[kk][0], qf4[kk][1], qf4[kk][2], qf4[kk][3], 0, 0, 0, 0};
+      s[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, s[blk], 4, 4, 0, ks[blk][kk], 0, qs4[kk]);
+    }
+  }
+}
+
+// The V operands (MXFP4 codes and scales) of an FP4 tile's P.V product.
+template <int D, int HPW>
+__device__ __forceinline__ void fp4_vops(const uint8_t *st, const int col, const int lh, int4v (&va)[D / 32],
+                                         int (&vs)[D / 32]) {
+  using T = Tile<D, HPW>;
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++) {
+    const int ch = 32 * cb + col;
+    va[cb] = *(const int4v *)(st + T::oV4 + ch * 32 + 16 * lh);
+    vs[cb] = st[T::oV4S + ch * 2 + lh];
+  }
+}
+
+// FP4 tile, first half: S^T (masked on the diagonal) and the V operands
+// (read here so their LDS latency hides under the softmax).
+template <int D, int HPW, bool MASK>
+__device__ __forceinline__ void fp4_scores(const uint8_t *st, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
+                                           const int col, const int lh, const int qpos, float16v (&s)[2],
+                                           int4v (&va)[D / 32], int (&vs)[D / 32]) {
+  fp4_qk<D, HPW>(st, qf4, qs4, col, lh, s);
+  fp4_vops<D, HPW>(st, col, lh, va, vs);
+  if (MASK) {
+#pragma unroll
+    for (int blk = 0; blk < 2; blk++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        if (32 * lh + 16 * blk + r > qpos) s[blk][r] = -INFINITY;
+  }
+}
+
+// FP4 tile, second half: p (this lane's 32 values, one aligned 32-key group,
+// relative to the max the exponent used) re-quantized to MXFP4, and
+// O^T += V^T P^T.  `shift` is an extra power of two folded into P's E8M0
+// scale (the group's contribution is exactly 2^shift times its codes).
+template <int CB>
+__device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax, const int shift,
+                                       const int4v (&va)[CB], const int (&vs)[CB], float16v (&acc)[CB]) {
+  const int psb = mx_scale_byte(amax);
+  const float div = mx_scale_divisor(psb);
+  uint32_t pw[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    const int blk = w >> 1, r0 = 8 * (w & 1);
+    THRIFT_CVT_FP4(pw[w], s[blk][r0 + 0], s[blk][r0 + 1], div, 0);
+    THRIFT_CVT_FP4(pw[w], s[blk][r0 + 2], s[blk][r0 + 3], div, 1);
+    THRIFT_CVT_FP4(pw[w], s[blk][r0 + 4], s[blk][r0 + 5], div, 2);
+    THRIFT_CVT_FP4(pw[w], s[blk][r0 + 6], s[blk][r0 + 7], div, 3);
+  }
+  int8v pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], 0, 0, 0, 0};
+  const int pscale = psb + shift;
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+    int8v a8 = {va[cb][0], va[cb][1], va[cb][2], va[cb][3], 0, 0, 0, 0};
+    acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, pb, acc[cb], 4, 4, 0, vs[cb], 0, pscale);
+  }
+}
+
+// One FP4 tile (general walk): the running max may rise, rescaling acc.
+template <int D, int HPW, bool MASK>
+__device__ __forceinline__ void tile_fp4(const uint8_t *st, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
+                                         float16v (&acc)[D / 32], float &M, float &l_part, float &mt_max,
+                                         const float c, const int col, const int lh, const int qpos) {
+  constexpr int CB = D / 32;
+  float16v s[2];
+  int4v va[CB];
+  int vs[CB];
+  fp4_scores<D, HPW, MASK>(st, qf4, qs4, col, lh, qpos, s, va, vs);
+  const float lane_max = softmax_step<CB, false>(s, acc, M, l_part, mt_max, c, lh, qpos);
+  fp4_pv<CB>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, -M)), 0, va, vs, acc);
+}
+
+// Softmax and P.V of one FP4-only tile whose scores s are already computed:
+// the accumulator is never rescaled here.  With the tile's integer max mt, p
+// is taken against Mp = max(M, mt - kLazy) (so p <= 2^kLazy) and the
+// difference Mp - M is folded into P's scale and into the row-sum increment.
+// A shift above kMaxShift sets `overflow` (the caller then redoes the work
+// item with M at the row's true max, where no shift occurs); the shift is
+// clamped meanwhile.
+template <int CB>
+__device__ __forceinline__ void fp4_fixed_rest(float16v (&s)[2], const int4v (&va)[CB], const int (&vs)[CB],
+                                               float16v (&acc)[CB], float &M, float &l_part, float &mt_max,
+                                               bool &overflow, const float c) {
+  const float lane_max = lane_max32(s);
+  const float mt = ceilf(fmaxf(lane_max, other_half(lane_max)) * c);
+  mt_max = fmaxf(mt_max, mt);
+  M = (M == -INFINITY) ? mt : M;  // a row whose first tile is FP4-only
+  float shift = fmaxf(M, mt - kLazy) - M;
+  overflow = overflow || shift > kMaxShift;
+  shift = fminf(shift, kMaxShift);
+  const float negM = -(M + shift);
+  float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    s[0][r] = __builtin_amdgcn_exp2f(fmaf(s[0][r], c, negM));
+    s[1][r] = __builtin_amdgcn_exp2f(fmaf(s[1][r], c, negM));
+    l0 += s[0][r];
+    l1 += s[1][r];
+  }
+  const int ish = (int)shift;
+  l_part = fmaf(l0 + l1, ldexpf(1.0f, ish), l_part);
+  fp4_pv<CB>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, negM)), ish, va, vs, acc);
+}
+
+// One FP16 tile for one wave: S^T from FP16 K and Q, P rounded to fp16,
+// O^T += V^T P^T with FP16 V.  qrow16 points at this lane's Q16 row in LDS.
+template <int D, int HPW, bool MASK>
+__device__ __forceinline__ void tile_fp16(const uint8_t *st, const uint8_t *qrow16, float16v (&acc)[D / 32],
+                                          float &M, float &l_part, float &mt_max, const float c, const int col,
+                                          const int lh, const int qpos) {
+  using T = Tile<D, HPW>;
+  constexpr int KS = D / 16, CB = D / 32, CPR = D / 8;  // k-steps, channel blocks, 16-byte chunks per row
+  float16v s[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; blk++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) s[blk][r] = 0.0f;
+  const int key0 = permuted_key(col, 0), key1 = permuted_key(col, 1);
+  const uint8_t *k0 = st + T::oK16 + key0 * (2 * D);
+  const uint8_t *k1 = st + T::oK16 + key1 * (2 * D);
+  const int sw0 = swz_k16<D>(key0), sw1 = swz_k16<D>(key1);
+#pragma unroll
+  for (int kk = 0; kk < KS; kk += 2) {
+    half8 qb[2], a0[2], a1[2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int chunk = 2 * (kk + u) + lh;
+      qb[u] = __builtin_bit_cast(half8, *(const int4v *)(qrow16 + 16 * (chunk ^ (col & (CPR - 1)))));
+      a0[u] = __builtin_bit_cast(half8, *(const int4v *)(k0 + 16 * (chunk ^ sw0)));
+      a1[u] = __builtin_bit_cast(half8, *(const int4v *)(k1 + 16 * (chunk ^ sw1)));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[u], qb[u], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[u], qb[u], s[1], 0, 0, 0);
+    }
+  }
+  softmax_step<CB, MASK>(s, acc, M, l_part, mt_max, c, lh, qpos);
+  // P in fp16; MFMA u consumes keys 32*lh + 8u + 0..7 of this lane
+  half8 pb[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+#pragma unroll
+    for (int t = 0; t < 8; t++) pb[u][t] = (_Float16)s[u >> 1][8 * (u & 1) + t];
+  const uint8_t *vt = st + T::oV16;
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+    const int ch = 32 * cb + col;
+    half8 vf[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      vf[u] = __builtin_bit_cast(half8, *(const int4v *)(vt + ch * 128 + 16 * ((4 * lh + u) ^ swz_v16(ch))));
+#pragma unroll
+    for (int u = 0; u < 4; u++) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[u], pb[u], acc[cb], 0, 0, 0);
+  }
+}
+
 template <int D, int HPW>
 __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
-  using T = Tile<D>;
+  using T = Tile<D, HPW>;
   constexpr int NT = 128 * HPW;                  // threads
-  constexpr int C4 = T::FP4_BYTES / 16;          // 16-byte chunks of the FP4 stage
-  constexpr int C16 = T::FP16_BYTES / 16;        // ... of the FP16 stage
-  constexpr int R4 = (C4 + NT - 1) / NT;         // chunks per thread
-  constexpr int R16 = (C16 + NT - 1) / NT;
-  constexpr int KS16 = D / 16;                   // k-steps of the FP16 QK product
   constexpr int KS4 = D / 64;                    // k-steps of the FP4 QK product
   constexpr int CB = D / 32;                     // 32-channel blocks of O^T
+  constexpr int CPR = D / 8;                     // 16-byte chunks per Q16 row
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint32_t *mask = (uint32_t *)(smem + 2 * T::STAGE);  // [HPW][kMaxBlocks/32] FP16-list bits
+  uint32_t *mask = (uint32_t *)(smem + T::oMASK);  // [HPW][kMaxBlocks/32] FP16-list bits
 
   const int nb = a.N / 64;
   const int group = a.Hq / a.Hkv;
@@ -94,6 +380,23 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
 
   // ---- FP16-list bitmask of each head of the workgroup
   for (int w = tid; w < HPW * nw; w += NT) mask[(w / nw) * (kMaxBlocks / 32) + w % nw] = 0;
+  // ---- this wave's 32 query rows: Q16 into LDS (swizzled), Q4 into registers
+  const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf;
+  uint8_t *q16w = smem + T::oQ16 + (size_t)wave * 32 * D * 2;
+#pragma unroll
+  for (int it = 0; it < CPR / 2; it++) {  // 32 rows x CPR chunks over 64 lanes
+    const int e = lane + 64 * it, row = e / CPR, ch = e % CPR;
+    const int4v v = *(const int4v *)(a.q16 + (qrow0 + row) * D + 8 * ch);
+    *(int4v *)(q16w + row * (2 * D) + 16 * (ch ^ (row & (CPR - 1)))) = v;
+  }
+  const int64_t qrow = qrow0 + col;
+  int4v qf4[KS4];
+  int qs4[KS4];
+#pragma unroll
+  for (int kk = 0; kk < KS4; kk++) {
+    qf4[kk] = *(const int4v *)(a.q4 + qrow * (D / 2) + 32 * kk + 16 * lh);
+    qs4[kk] = a.q4s[qrow * (D / 32) + 2 * kk + lh];
+  }
   __syncthreads();
   const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
   const int64_t roff = a.causal ? (int64_t)i * (i + 1) / 2 : (int64_t)i * nb;
@@ -114,250 +417,224 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     uint32_t m = 0;
 #pragma unroll
     for (int h = 0; h < HPW; h++) m |= ((mask[h * (kMaxBlocks / 32) + (j >> 5)] >> (j & 31)) & 1u) << h;
-    return m & head_bits;
+    return (uint32_t)__builtin_amdgcn_readfirstlane(m & head_bits);
   };
 
-  // ---- this wave's queries: Q16 and Q4 B-operands, held in registers
-  const int64_t qrow = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf + col;
-  half8 qf16[KS16];
-  int4v qf4[KS4];
-  int qs4[KS4];
-#pragma unroll
-  for (int kk = 0; kk < KS16; kk++)
-    qf16[kk] = __builtin_bit_cast(half8, *(const int4v *)(a.q16 + qrow * D + 16 * kk + 8 * lh));
-#pragma unroll
-  for (int kk = 0; kk < KS4; kk++) {
-    qf4[kk] = *(const int4v *)(a.q4 + qrow * (D / 2) + 32 * kk + 16 * lh);
-    qs4[kk] = a.q4s[qrow * (D / 32) + 2 * kk + lh];
-  }
-
-  // ---- K/V tile sources
+  // ---- K/V tile loads: direct global -> LDS copies (global_load_lds_dwordx4;
+  // lane L of a wave writes its 16 bytes at the wave-uniform LDS base + 16 L).
+  // Each wave copies whole 1 KB groups of one region, so the region choice is
+  // scalar and the source address is a scalar base plus a per-lane offset
+  // (with the chunk swizzle of the region).  The caller waits (vmcnt) before
+  // the barrier that publishes the stage.
+  constexpr int NWAVES = 2 * HPW;
   const int64_t kvh = (int64_t)b * a.Hkv + g;
-  auto fp4_src = [&](int j, int c) -> const int4v * {
-    const int off = 16 * c;
-    if (off < T::oK4S) return (const int4v *)(a.k4 + (kvh * a.N + 64 * (int64_t)j) * (D / 2) + off);
-    if (off < T::oV4) return (const int4v *)(a.k4s + (kvh * a.N + 64 * (int64_t)j) * (D / 32) + (off - T::oK4S));
-    if (off < T::oV4S) return (const int4v *)(a.v4 + (kvh * nb + j) * (int64_t)(32 * D) + (off - T::oV4));
-    return (const int4v *)(a.v4s + (kvh * nb + j) * (int64_t)(2 * D) + (off - T::oV4S));
-  };
-  auto fp16_src = [&](int j, int c) -> const int4v * {
-    const int off = 16 * c;
-    if (off < T::K16) return (const int4v *)((const uint8_t *)a.k16 + (kvh * a.N + 64 * (int64_t)j) * (2 * D) + off);
-    return (const int4v *)((const uint8_t *)a.v16 + (kvh * nb + j) * (int64_t)(128 * D) + (off - T::K16));
-  };
-  int4v pre4[R4], pre16[R16];
-  auto prefetch = [&](int j, uint32_t h16) {
-    const bool need16 = h16 != 0, need4 = h16 != head_bits;
-    if (need4) {
-#pragma unroll
-      for (int r = 0; r < R4; r++) {
-        const int c = tid + r * NT;
-        if (c < C4) pre4[r] = *fp4_src(j, c);
+  const uint8_t *k4b = a.k4 + kvh * a.N * (D / 2), *k4sb = a.k4s + kvh * a.N * (D / 32);
+  const uint8_t *v4b = a.v4 + kvh * nb * (int64_t)(32 * D), *v4sb = a.v4s + kvh * nb * (int64_t)(2 * D);
+  const uint8_t *k16b = (const uint8_t *)a.k16 + kvh * a.N * (2 * D);
+  const uint8_t *v16b = (const uint8_t *)a.v16 + kvh * nb * (int64_t)(128 * D);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue_loads = [&](uint8_t *st, int j, uint32_t h16) {
+    if (h16 != head_bits) {
+      for (int t = wave_u; t < T::G4; t += NWAVES) {
+        const uint8_t *src;
+        if (t < T::K4 / 1024) {
+          const int off = 1024 * t + 16 * lane, key = off / (D / 2), pch = (off % (D / 2)) / 16;
+          src = k4b + (int64_t)j * (64 * D / 2) + key * (D / 2) + 16 * (pch ^ swz_k4<D>(key));
+        } else {
+          src = v4b + (int64_t)j * (32 * D) + 1024 * (t - T::K4 / 1024) + 16 * lane;
+        }
+        load_to_lds(src, st + 1024 * t);
+      }
+      if (wave_u == NWAVES - 1 && lane < T::SC4) {
+        const uint8_t *src = lane < T::K4S / 16 ? k4sb + (int64_t)j * (64 * D / 32) + 16 * lane
+                                                : v4sb + (int64_t)j * (2 * D) + 16 * (lane - T::K4S / 16);
+        load_to_lds(src, st + T::oK4S);
       }
     }
-    if (need16) {
-#pragma unroll
-      for (int r = 0; r < R16; r++) {
-        const int c = tid + r * NT;
-        if (c < C16) pre16[r] = *fp16_src(j, c);
-      }
-    }
-  };
-  auto commit = [&](uint8_t *st, uint32_t h16) {
-    const bool need16 = h16 != 0, need4 = h16 != head_bits;
-    if (need4) {
-#pragma unroll
-      for (int r = 0; r < R4; r++) {
-        const int c = tid + r * NT;
-        if (c < C4) *(int4v *)(st + 16 * c) = pre4[r];
-      }
-    }
-    if (need16) {
-#pragma unroll
-      for (int r = 0; r < R16; r++) {
-        const int c = tid + r * NT;
-        if (c < C16) *(int4v *)(st + T::FP4_BYTES + 16 * c) = pre16[r];
+    if (h16 != 0) {
+      for (int t = wave_u; t < T::G16; t += NWAVES) {
+        const uint8_t *src;
+        if (t < T::K16 / 1024) {
+          const int off = 1024 * t + 16 * lane, key = off / (2 * D), pch = (off % (2 * D)) / 16;
+          src = k16b + (int64_t)j * (64 * 2 * D) + key * (2 * D) + 16 * (pch ^ swz_k16<D>(key));
+        } else {
+          const int o = 1024 * (t - T::K16 / 1024) + 16 * lane, ch = o / 128, pch = (o % 128) / 16;
+          src = v16b + (int64_t)j * (128 * D) + ch * 128 + 16 * (pch ^ swz_v16(ch));
+        }
+        load_to_lds(src, st + T::oK16 + 1024 * t);
       }
     }
   };
 
-  // ---- softmax state and accumulators
-  float16v acc[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) acc[cb][r] = 0.0f;
-  float M = -INFINITY, l_part = 0.0f;
   const float c = a.c;
   const int qpos = 32 * qhalf + col;  // query row inside the block
+  const uint8_t *qrow16 = q16w + col * (2 * D);
 
-  uint32_t h16_cur = fp16_heads(0);
-  prefetch(0, h16_cur);
-  commit(smem, h16_cur);
+  // ---- traversal.  Phase 1 walks the union of the heads' FP16 lists (all
+  // FP16 tiles, the first and the diagonal block), where the row max is
+  // almost always reached; phase 2 walks the blocks every head has on its
+  // FP4 list, with the accumulator left unscaled (fp4_fixed_rest).  Both
+  // walks are ascending and prefetch ahead of the tile being computed.
+  uint32_t *umask = (uint32_t *)(smem + T::oUMASK);
+  for (int w = tid; w < nw; w += NT) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int h = 0; h < HPW; h++)
+      if ((head_bits >> h) & 1u) u |= mask[h * (kMaxBlocks / 32) + w];
+    umask[w] = u;
+  }
   __syncthreads();
+  // Causal rows end at the diagonal block, which takes the masked bodies and
+  // is handled on its own between the two walks (so neither walk's loop body
+  // branches on it).
+  const int jend = a.causal ? nv - 1 : nv;  // walks cover [0, jend)
+  auto next_tile = [&](int j, bool in16) -> int {  // smallest j' >= j of the walk's set below jend, else nv
+    for (int w = j >> 5; w < nw; w++) {
+      uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane(umask[w]);
+      if (!in16) m = ~m;
+      if (w == (j >> 5)) m &= ~0u << (j & 31);
+      if (m) {
+        const int jj = 32 * w + __builtin_ctz(m);
+        return jj < jend ? jj : nv;
+      }
+    }
+    return nv;
+  };
 
-  for (int j = 0; j < nv; j++) {
-    const uint8_t *st = smem + (j & 1) * T::STAGE;
-    uint32_t h16_next = 0;
-    if (j + 1 < nv) {
-      h16_next = fp16_heads(j + 1);
-      prefetch(j + 1, h16_next);
-    }
-    if (head_ok) {
-      const bool use16 = (h16_cur >> hl) & 1u;
-      const bool diag = a.causal && (j == i);
-      // S^T = K Q^T for the two 32-key halves of the permuted tile
-      float16v s[2];
+  // Pass 0 normally finishes the work item.  If a phase-2 tile needed a
+  // shift beyond kMaxShift in some row, the workgroup makes pass 1 with every
+  // row's M preset to its true integer max (tracked in pass 0): no tile can
+  // then raise M, and pass 1 always finishes.
+  float mt_max = -INFINITY;
+  for (int pass = 0; pass < 2; pass++) {
+    float16v acc[CB];
 #pragma unroll
-      for (int blk = 0; blk < 2; blk++) {
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) s[blk][r] = 0.0f;
-        const int key = permuted_key(col, blk);
-        if (use16) {
-          const uint8_t *krow = st + T::oK16 + key * (2 * D);
-#pragma unroll
-          for (int kk = 0; kk < KS16; kk++) {
-            half8 kf = __builtin_bit_cast(half8, *(const int4v *)(krow + 2 * (16 * kk + 8 * lh)));
-            s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf16[kk], s[blk], 0, 0, 0);
-          }
-        } else {
-          const uint8_t *krow = st + T::oK4 + key * (D / 2);
-          const uint8_t *ksc = st + T::oK4S + key * (D / 32);
-#pragma unroll
-          for (int kk = 0; kk < KS4; kk++) {
-            int4v kf = *(const int4v *)(krow + 32 * kk + 16 * lh);
-            int8v ka = {kf[0], kf[1], kf[2], kf[3], 0, 0, 0, 0};
-            int8v qb = {qf4[kk][0], qf4[kk][1], qf4[kk][2], qf4[kk][3], 0, 0, 0, 0};
-            s[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qb, s[blk], 4, 4, 0, (int)ksc[2 * kk + lh], 0,
-                                                                      qs4[kk]);
-          }
-        }
-      }
-      // causal mask: key 32*lh + idx of this lane vs query qpos
-      if (diag) {
-#pragma unroll
-        for (int blk = 0; blk < 2; blk++)
-#pragma unroll
-          for (int r = 0; r < 16; r++)
-            if (32 * lh + 16 * blk + r > qpos) s[blk][r] = -INFINITY;
-      }
-      // row max over this lane's 32 keys, then over the partner lane's
-      float smax = -INFINITY;
-#pragma unroll
-      for (int blk = 0; blk < 2; blk++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) smax = fmaxf(smax, s[blk][r]);
-      const float lane_max = smax;
-      smax = fmaxf(smax, __shfl_xor(smax, 32));
-      const float mt = ceilf(smax * c);  // integer candidate max (log2 units)
-      const bool raise = mt > M + kLazy || M == -INFINITY;
-      if (__any(raise)) {
-        if (raise) {
-          const float sc = (M == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(M - mt));
-          l_part *= sc;
-#pragma unroll
-          for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) acc[cb][r] *= sc;
-          M = mt;
-        }
-      }
-      const float negM = -M;
-      // p = 2^(x - M); masked keys give 2^-inf = 0
-      float lsum = 0.0f;
-#pragma unroll
-      for (int blk = 0; blk < 2; blk++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[blk][r], c, negM));
-          s[blk][r] = p;
-          lsum += p;
-        }
-      l_part += lsum;
-      if (use16) {
-        // P in fp16; MFMA u consumes keys 32*lh + 8u + 0..7 of this lane
-        half8 pb[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-#pragma unroll
-          for (int t = 0; t < 8; t++) pb[u][t] = (_Float16)s[u >> 1][8 * (u & 1) + t];
-        const uint8_t *vt = st + T::oV16;
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++) {
-          const int ch = 32 * cb + col;
-#pragma unroll
-          for (int u = 0; u < 4; u++) {
-            half8 vf = __builtin_bit_cast(half8, *(const int4v *)(vt + ch * 128 + 2 * (32 * lh + 8 * u)));
-            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb[u], acc[cb], 0, 0, 0);
-          }
-        }
-      } else {
-        // P re-quantized to MXFP4: this lane's 32 values are one aligned group
-        const float amax = __builtin_amdgcn_exp2f(fmaf(lane_max, c, negM));
-        const int psb = mx_scale_byte(amax);
-        const float div = mx_scale_divisor(psb);
-        uint32_t pw[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int w = 0; w < 4; w++) {
-          const int blk = w >> 1, r0 = 8 * (w & 1);
-          THRIFT_CVT_FP4(pw[w], s[blk][r0 + 0], s[blk][r0 + 1], div, 0);
-          THRIFT_CVT_FP4(pw[w], s[blk][r0 + 2], s[blk][r0 + 3], div, 1);
-          THRIFT_CVT_FP4(pw[w], s[blk][r0 + 4], s[blk][r0 + 5], div, 2);
-          THRIFT_CVT_FP4(pw[w], s[blk][r0 + 6], s[blk][r0 + 7], div, 3);
-        }
-        int8v pbv = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], 0, 0, 0, 0};
-        const uint8_t *vt = st + T::oV4;
-        const uint8_t *vs = st + T::oV4S;
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++) {
-          const int ch = 32 * cb + col;
-          int4v vf = *(const int4v *)(vt + ch * 32 + 16 * lh);
-          int8v va = {vf[0], vf[1], vf[2], vf[3], 0, 0, 0, 0};
-          acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pbv, acc[cb], 4, 4, 0, (int)vs[ch * 2 + lh], 0,
-                                                                     psb);
-        }
-      }
-    }
-    if (j + 1 < nv) commit(smem + ((j + 1) & 1) * T::STAGE, h16_next);
-    h16_cur = h16_next;
+      for (int r = 0; r < 16; r++) acc[cb][r] = 0.0f;
+    float M = pass == 0 ? -INFINITY : mt_max, l_part = 0.0f;
+    bool overflow = false;
+
+    // tile order: phase-1 tiles, the diagonal (causal), phase-2 tiles
+    int j = next_tile(0, true);
+    if (j >= nv) j = a.causal ? nv - 1 : nv;
+    uint32_t h16_cur = (j < nv) ? fp16_heads(j) : 0u;
+    int par = 0;
+    if (j < nv) issue_loads(smem, j, h16_cur);
+    wait_vmem();
     __syncthreads();
-  }
+    // phase 1 (below the diagonal)
+    while (j < jend) {
+      int jn = next_tile(j + 1, true);
+      if (jn >= nv) jn = a.causal ? nv - 1 : nv;
+      const uint32_t h16_next = (jn < nv) ? fp16_heads(jn) : 0u;
+      if (jn < nv) issue_loads(smem + (par ^ 1) * T::STAGE, jn, h16_next);
+      const uint8_t *st = smem + par * T::STAGE;
+      if (head_ok) {
+        if ((h16_cur >> hl) & 1u)
+          tile_fp16<D, HPW, false>(st, qrow16, acc, M, l_part, mt_max, c, col, lh, qpos);
+        else
+          tile_fp4<D, HPW, false>(st, qf4, qs4, acc, M, l_part, mt_max, c, col, lh, qpos);
+      }
+      wait_vmem();
+      __syncthreads();
+      par ^= 1;
+      j = jn;
+      h16_cur = h16_next;
+    }
+    // the diagonal tile (causal)
+    if (j < nv) {
+      const uint8_t *st = smem + par * T::STAGE;
+      if (head_ok) {
+        if ((h16_cur >> hl) & 1u)
+          tile_fp16<D, HPW, true>(st, qrow16, acc, M, l_part, mt_max, c, col, lh, qpos);
+        else
+          tile_fp4<D, HPW, true>(st, qf4, qs4, acc, M, l_part, mt_max, c, col, lh, qpos);
+      }
+      __syncthreads();
+    }
+    // Phase 2 (below the diagonal): every head computes these in FP4.  A
+    // 3-slot ring of FP4 stages (reusing the stage memory): while tile k is
+    // in softmax/P.V, the QK MFMAs of tile k+1 are already issued and tile
+    // k+2 is loading.  The loop is unrolled over the ring period so every LDS
+    // offset is a constant.
+    {
+      int jc = next_tile(0, false);
+      int jn = (jc < nv) ? next_tile(jc + 1, false) : nv;
+      if (jc < nv) issue_loads(smem, jc, 0u);
+      if (jn < nv) issue_loads(smem + T::RING, jn, 0u);
+      wait_vmem();
+      __syncthreads();
+      float16v sa[2], sb[2];
+      if (jc < nv && head_ok) fp4_qk<D, HPW>(smem, qf4, qs4, col, lh, sa);
+      auto step = [&](const int cur, const int nxt, const int ldslot, float16v (&s_in)[2], float16v (&s_out)[2]) {
+        const int jnn = (jn < nv) ? next_tile(jn + 1, false) : nv;
+        if (jnn < nv) issue_loads(smem + ldslot * T::RING, jnn, 0u);
+        if (head_ok) {
+          if (jn < nv) fp4_qk<D, HPW>(smem + nxt * T::RING, qf4, qs4, col, lh, s_out);
+          int4v va[CB];
+          int vs[CB];
+          fp4_vops<D, HPW>(smem + cur * T::RING, col, lh, va, vs);
+          fp4_fixed_rest<CB>(s_in, va, vs, acc, M, l_part, mt_max, overflow, c);
+        }
+        wait_vmem();
+        __syncthreads();
+        jc = jn;
+        jn = jnn;
+      };
+      while (jc < nv) {
+        step(0, 1, 2, sa, sb);
+        if (jc >= nv) break;
+        step(1, 2, 0, sb, sa);
+        if (jc >= nv) break;
+        step(2, 0, 1, sa, sb);
+        if (jc >= nv) break;
+        step(0, 1, 2, sb, sa);
+        if (jc >= nv) break;
+        step(1, 2, 0, sa, sb);
+        if (jc >= nv) break;
+        step(2, 0, 1, sb, sa);
+      }
+    }
+    if (pass == 0 && __syncthreads_or(overflow ? 1 : 0)) continue;
 
-  // ---- epilogue: O = acc / l, lse = (M + log2 l) ln 2
-  if (!head_ok) return;
-  const float l = l_part + __shfl_xor(l_part, 32);
-  const float inv = 1.0f / l;
+    // ---- epilogue: O = acc / l, lse = (M + log2 l) ln 2
+    if (!head_ok) return;
+    const float l = l_part + other_half(l_part);
+    const float inv = 1.0f / l;
 #pragma unroll
-  for (int cb = 0; cb < CB; cb++) {
+    for (int cb = 0; cb < CB; cb++) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; q4++) {
-      const int ch = 32 * cb + 8 * q4 + 4 * lh;  // rows 8(r/4) + 4(lane/32) + r%4 of block cb
-      float4v o = {acc[cb][4 * q4 + 0] * inv, acc[cb][4 * q4 + 1] * inv, acc[cb][4 * q4 + 2] * inv,
-                   acc[cb][4 * q4 + 3] * inv};
-      if (a.out_dtype == 2) {
-        *(float4v *)((float *)a.out + qrow * D + ch) = o;
-      } else if (a.out_dtype == 0) {
-        _Float16 *op = (_Float16 *)a.out + qrow * D + ch;
-        for (int e = 0; e < 4; e++) op[e] = (_Float16)o[e];
-      } else {
-        uint16_t *op = (uint16_t *)a.out + qrow * D + ch;
-        for (int e = 0; e < 4; e++) {
-          uint32_t u = __float_as_uint(o[e]);
-          u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even (finite values)
-          op[e] = (uint16_t)(u >> 16);
+      for (int q4 = 0; q4 < 4; q4++) {
+        const int ch = 32 * cb + 8 * q4 + 4 * lh;  // rows 8(r/4) + 4(lane/32) + r%4 of block cb
+        float4v o = {acc[cb][4 * q4 + 0] * inv, acc[cb][4 * q4 + 1] * inv, acc[cb][4 * q4 + 2] * inv,
+                     acc[cb][4 * q4 + 3] * inv};
+        if (a.out_dtype == 2) {
+          *(float4v *)((float *)a.out + qrow * D + ch) = o;
+        } else if (a.out_dtype == 0) {
+          _Float16 *op = (_Float16 *)a.out + qrow * D + ch;
+          for (int e = 0; e < 4; e++) op[e] = (_Float16)o[e];
+        } else {
+          uint16_t *op = (uint16_t *)a.out + qrow * D + ch;
+          for (int e = 0; e < 4; e++) {
+            uint32_t u = __float_as_uint(o[e]);
+            u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even (finite values)
+            op[e] = (uint16_t)(u >> 16);
+          }
         }
       }
     }
+    if (a.lse && lh == 0) a.lse[qrow] = (M + __log2f(l)) * 0.69314718055994530942f;
+    return;
   }
-  if (a.lse && lh == 0) a.lse[qrow] = (M + __log2f(l)) * 0.69314718055994530942f;
 }
 
 template <int D, int HPW>
 static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
-  using T = Tile<D>;
+  using T = Tile<D, HPW>;
   const int group = a.Hq / a.Hkv;
   const int chunks = (group + HPW - 1) / HPW;
-  const size_t lds = 2 * (size_t)T::STAGE + (size_t)HPW * (kMaxBlocks / 32) * 4;
+  const size_t lds = (size_t)T::LDS;
   hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
