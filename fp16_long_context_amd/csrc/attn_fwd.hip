@@ -36,10 +36,10 @@
 namespace thrift {
 
 constexpr float kLazy = 8.0f;
-// Largest power-of-two shift an FP4-only tile may fold into P's scale.  With
-// |v| <= 2^16, at most 2^19 keys and p <= 2^kLazy, acc stays below
-// 2^(64 + 8 + 16 + 19) = 2^107 and P's scale byte below 133 + 64 = 197.
-constexpr float kMaxShift = 64.0f;
+// Largest p an FP4-only tile may reach against the running max (2^64).
+// With |v| <= 2^16 and at most 2^19 keys, acc stays below 2^(64 + 16 + 19)
+// = 2^99 and P's scale byte at most 127 + 64 - 2 = 189.
+constexpr float kMaxP = 0x1p64f;
 
 template <int D, int HPW>
 struct Tile {
@@ -73,17 +73,20 @@ struct Tile {
 // rows, at the same logical chunk) spread over all LDS banks.  Physical chunk
 // = logical chunk ^ swz(row).  The loader applies the same map to the source
 // address, so the direct global->LDS copy stays a plain per-lane transfer.
+// The maps keep every group of 8 lanes (128 bytes) and of 16 lanes (256
+// bytes) of an operand read on distinct bank slots.
 template <int D>
 __device__ __forceinline__ int swz_k4(int key) {  // K4 rows: D/32 chunks
-  if (D == 128) return ((key >> 2) & 1) | (((key >> 5) & 1) << 1);
+  if (D == 128) return (((key >> 1) ^ (key >> 2)) & 1) | (((key >> 5) & 1) << 1);
   return (key >> 5) & 1;
 }
 template <int D>
 __device__ __forceinline__ int swz_k16(int key) {  // K16 rows: D/8 chunks
-  if (D == 128) return (key & 3) | (((key >> 2) & 1) << 2) | (((key >> 5) & 1) << 3);
+  if (D == 128) return (key & 3) | (((key >> 5) & 1) << 2) | (((key >> 2) & 1) << 3);
   return ((key >> 1) & 1) | (((key >> 2) & 1) << 1) | (((key >> 5) & 1) << 2);
 }
-__device__ __forceinline__ int swz_v16(int ch) { return (ch >> 1) & 7; }  // V16 rows: 8 chunks
+__device__ __forceinline__ int swz_v16(int ch) { return (ch ^ (ch >> 3)) & 7; }       // V16 rows: 8 chunks
+__device__ __forceinline__ int swz_v4(int ch) { return ((ch >> 2) ^ (ch >> 3)) & 1; }  // V4 rows: 2 chunks
 
 // Key (row of the 64-key tile) that A-operand row rho of MFMA block blk
 // reads, so that the result lands in the lane layout described above.
@@ -109,13 +112,15 @@ __device__ __forceinline__ float other_half(float x) {
 
 // Largest of this lane's 32 scores (v_max3 chain).
 __device__ __forceinline__ float lane_max32(const float16v (&s)[2]) {
-  float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);
+  float m[4] = {fmaxf(s[0][0], s[0][1]), fmaxf(s[0][8], s[0][9]), fmaxf(s[1][0], s[1][1]), fmaxf(s[1][8], s[1][9])};
 #pragma unroll
-  for (int r = 2; r < 16; r += 2) {
-    m0 = fmaxf(fmaxf(m0, s[0][r]), s[0][r + 1]);
-    m1 = fmaxf(fmaxf(m1, s[1][r]), s[1][r + 1]);
+  for (int r = 2; r < 8; r += 2) {
+    m[0] = fmaxf(fmaxf(m[0], s[0][r]), s[0][r + 1]);
+    m[1] = fmaxf(fmaxf(m[1], s[0][8 + r]), s[0][9 + r]);
+    m[2] = fmaxf(fmaxf(m[2], s[1][r]), s[1][r + 1]);
+    m[3] = fmaxf(fmaxf(m[3], s[1][8 + r]), s[1][9 + r]);
   }
-  return fmaxf(m0, m1);
+  return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
 }
 
 // Online-softmax step on one 32-query x 64-key score tile held as s[2]
@@ -126,7 +131,7 @@ __device__ __forceinline__ float lane_max32(const float16v (&s)[2]) {
 // largest raw score (-inf if all masked).
 template <int CB, bool MASK>
 __device__ __forceinline__ float softmax_step(float16v (&s)[2], float16v (&acc)[CB], float &M, float &l_part,
-                                              float &mt_max, const float c, const int lh, const int qpos) {
+                                              const float c, const int lh, const int qpos) {
   if (MASK) {
 #pragma unroll
     for (int blk = 0; blk < 2; blk++)
@@ -137,7 +142,6 @@ __device__ __forceinline__ float softmax_step(float16v (&s)[2], float16v (&acc)[
   const float lane_max = lane_max32(s);
   const float row_max = fmaxf(lane_max, other_half(lane_max));
   const float mt = ceilf(row_max * c);  // integer candidate max (log2 units)
-  mt_max = fmaxf(mt_max, mt);
   const bool raise = (mt > M + kLazy) || (M == -INFINITY);
   if (__ballot(raise)) {  // wave-uniform; lanes that keep their max scale by 1
     const float sc = raise ? ((M == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(M - mt))) : 1.0f;
@@ -161,34 +165,48 @@ __device__ __forceinline__ float softmax_step(float16v (&s)[2], float16v (&acc)[
   return lane_max;
 }
 
-// S^T = K4 Q4^T of an FP4 tile for the two 32-key halves of the permuted tile.
+// K operands (MXFP4 codes and scale bytes) of an FP4 tile's QK product.
 template <int D, int HPW>
-__device__ __forceinline__ void fp4_qk(const uint8_t *st, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
-                                       const int col, const int lh, float16v (&s)[2]) {
+__device__ __forceinline__ void fp4_kops(const uint8_t *st, const int col, const int lh, int4v (&ka)[2][D / 64],
+                                         int (&ks)[2][D / 64]) {
   using T = Tile<D, HPW>;
-  constexpr int KS = D / 64;
-  int4v ka[2][KS];
-  int ks[2][KS];
 #pragma unroll
   for (int blk = 0; blk < 2; blk++) {
     const int key = permuted_key(col, blk);
 #pragma unroll
-    for (int kk = 0; kk < KS; kk++) {
+    for (int kk = 0; kk < D / 64; kk++) {
       ka[blk][kk] = *(const int4v *)(st + T::oK4 + key * (D / 2) + 16 * ((2 * kk + lh) ^ swz_k4<D>(key)));
       ks[blk][kk] = st[T::oK4S + key * (D / 32) + 2 * kk + lh];
     }
   }
+}
+
+// S^T = K4 Q4^T for the two 32-key halves of the permuted tile.
+template <int D>
+__device__ __forceinline__ void fp4_qk_mfma(const int4v (&ka)[2][D / 64], const int (&ks)[2][D / 64],
+                                            const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
+                                            float16v (&s)[2]) {
 #pragma unroll
   for (int blk = 0; blk < 2; blk++) {
 #pragma unroll
     for (int r = 0; r < 16; r++) s[blk][r] = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < KS; kk++) {
+    for (int kk = 0; kk < D / 64; kk++) {
       int8v a8 = {ka[blk][kk][0], ka[blk][kk][1], ka[blk][kk][2], ka[blk][kk][3], 0, 0, 0, 0};
       int8v b8 = {qf4[kk][0], qf4[kk][1], qf4[kk][2], qf4[kk][3], 0, 0, 0, 0};
       s[blk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, s[blk], 4, 4, 0, ks[blk][kk], 0, qs4[kk]);
     }
   }
+}
+
+// S^T = K4 Q4^T of an FP4 tile (operand reads + MFMAs).
+template <int D, int HPW>
+__device__ __forceinline__ void fp4_qk(const uint8_t *st, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
+                                       const int col, const int lh, float16v (&s)[2]) {
+  int4v ka[2][D / 64];
+  int ks[2][D / 64];
+  fp4_kops<D, HPW>(st, col, lh, ka, ks);
+  fp4_qk_mfma<D>(ka, ks, qf4, qs4, s);
 }
 
 // The V operands (MXFP4 codes and scales) of an FP4 tile's P.V product.
@@ -199,7 +217,7 @@ __device__ __forceinline__ void fp4_vops(const uint8_t *st, const int col, const
 #pragma unroll
   for (int cb = 0; cb < D / 32; cb++) {
     const int ch = 32 * cb + col;
-    va[cb] = *(const int4v *)(st + T::oV4 + ch * 32 + 16 * lh);
+    va[cb] = *(const int4v *)(st + T::oV4 + ch * 32 + 16 * (lh ^ swz_v4(ch)));
     vs[cb] = st[T::oV4S + ch * 2 + lh];
   }
 }
@@ -251,36 +269,29 @@ __device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
 // One FP4 tile (general walk): the running max may rise, rescaling acc.
 template <int D, int HPW, bool MASK>
 __device__ __forceinline__ void tile_fp4(const uint8_t *st, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
-                                         float16v (&acc)[D / 32], float &M, float &l_part, float &mt_max,
-                                         const float c, const int col, const int lh, const int qpos) {
+                                         float16v (&acc)[D / 32], float &M, float &l_part, const float c,
+                                         const int col, const int lh, const int qpos) {
   constexpr int CB = D / 32;
   float16v s[2];
   int4v va[CB];
   int vs[CB];
   fp4_scores<D, HPW, MASK>(st, qf4, qs4, col, lh, qpos, s, va, vs);
-  const float lane_max = softmax_step<CB, false>(s, acc, M, l_part, mt_max, c, lh, qpos);
+  const float lane_max = softmax_step<CB, false>(s, acc, M, l_part, c, lh, qpos);
   fp4_pv<CB>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, -M)), 0, va, vs, acc);
 }
 
-// Softmax and P.V of one FP4-only tile whose scores s are already computed:
-// the accumulator is never rescaled here.  With the tile's integer max mt, p
-// is taken against Mp = max(M, mt - kLazy) (so p <= 2^kLazy) and the
-// difference Mp - M is folded into P's scale and into the row-sum increment.
-// A shift above kMaxShift sets `overflow` (the caller then redoes the work
-// item with M at the row's true max, where no shift occurs); the shift is
-// clamped meanwhile.
+// Softmax and P.V of one FP4-only tile whose scores s are already computed.
+// The running max M is final for this walk (it was set by the FP16-union
+// walk and the diagonal): p = 2^(s*c - M) is taken directly, so no step of
+// the exponentials waits on this tile's max.  P's group scale comes from the
+// largest p of the lane's 32-key group (the MXFP4 rule's amax, taken after
+// the exponentials); a group with amax above kMaxP (or infinite) sets
+// `overflow`, and the work item is then redone with the rescaling walk.
 template <int CB>
 __device__ __forceinline__ void fp4_fixed_rest(float16v (&s)[2], const int4v (&va)[CB], const int (&vs)[CB],
-                                               float16v (&acc)[CB], float &M, float &l_part, float &mt_max,
-                                               bool &overflow, const float c) {
-  const float lane_max = lane_max32(s);
-  const float mt = ceilf(fmaxf(lane_max, other_half(lane_max)) * c);
-  mt_max = fmaxf(mt_max, mt);
-  M = (M == -INFINITY) ? mt : M;  // a row whose first tile is FP4-only
-  float shift = fmaxf(M, mt - kLazy) - M;
-  overflow = overflow || shift > kMaxShift;
-  shift = fminf(shift, kMaxShift);
-  const float negM = -(M + shift);
+                                               float16v (&acc)[CB], const float M, float &l_part, bool &overflow,
+                                               const float c) {
+  const float negM = -M;
   float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
@@ -289,17 +300,18 @@ __device__ __forceinline__ void fp4_fixed_rest(float16v (&s)[2], const int4v (&v
     l0 += s[0][r];
     l1 += s[1][r];
   }
-  const int ish = (int)shift;
-  l_part = fmaf(l0 + l1, ldexpf(1.0f, ish), l_part);
-  fp4_pv<CB>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, negM)), ish, va, vs, acc);
+  l_part += l0 + l1;
+  const float amax = lane_max32(s);
+  overflow = overflow || !(amax <= kMaxP);
+  fp4_pv<CB>(s, amax, 0, va, vs, acc);
 }
 
 // One FP16 tile for one wave: S^T from FP16 K and Q, P rounded to fp16,
 // O^T += V^T P^T with FP16 V.  qrow16 points at this lane's Q16 row in LDS.
 template <int D, int HPW, bool MASK>
 __device__ __forceinline__ void tile_fp16(const uint8_t *st, const uint8_t *qrow16, float16v (&acc)[D / 32],
-                                          float &M, float &l_part, float &mt_max, const float c, const int col,
-                                          const int lh, const int qpos) {
+                                          float &M, float &l_part, const float c, const int col, const int lh,
+                                          const int qpos) {
   using T = Tile<D, HPW>;
   constexpr int KS = D / 16, CB = D / 32, CPR = D / 8;  // k-steps, channel blocks, 16-byte chunks per row
   float16v s[2];
@@ -327,7 +339,7 @@ __device__ __forceinline__ void tile_fp16(const uint8_t *st, const uint8_t *qrow
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[u], qb[u], s[1], 0, 0, 0);
     }
   }
-  softmax_step<CB, MASK>(s, acc, M, l_part, mt_max, c, lh, qpos);
+  softmax_step<CB, MASK>(s, acc, M, l_part, c, lh, qpos);
   // P in fp16; MFMA u consumes keys 32*lh + 8u + 0..7 of this lane
   half8 pb[4];
 #pragma unroll
@@ -433,6 +445,38 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   const uint8_t *k16b = (const uint8_t *)a.k16 + kvh * a.N * (2 * D);
   const uint8_t *v16b = (const uint8_t *)a.v16 + kvh * nb * (int64_t)(128 * D);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // FP4-only walk: this wave's code groups t = wave_u + g * NWAVES (< G4)
+  // have fixed per-lane offsets inside a tile; per tile only the scalar base
+  // moves (j times the array's per-block stride).
+  constexpr int NG4 = (T::G4 + NWAVES - 1) / NWAVES;
+  uint32_t goff[NG4];
+#pragma unroll
+  for (int g = 0; g < NG4; g++) {
+    const int t = wave_u + g * NWAVES;
+    if (t < T::K4 / 1024) {
+      const int off = 1024 * t + 16 * lane, key = off / (D / 2), pch = (off % (D / 2)) / 16;
+      goff[g] = key * (D / 2) + 16 * (pch ^ swz_k4<D>(key));
+    } else {
+      const int o = 1024 * (t - T::K4 / 1024) + 16 * lane, ch = o / 32, pch = (o % 32) / 16;
+      goff[g] = ch * 32 + 16 * (pch ^ swz_v4(ch));
+    }
+  }
+  auto issue_fp4 = [&](uint8_t *st, int j) {
+#pragma unroll
+    for (int g = 0; g < NG4; g++) {
+      const int t = wave_u + g * NWAVES;
+      if (t < T::G4) {
+        const uint8_t *base = (t < T::K4 / 1024) ? k4b + (int64_t)j * (64 * D / 2) : v4b + (int64_t)j * (32 * D);
+        load_to_lds(base + goff[g], st + 1024 * t);
+      }
+    }
+    if (wave_u == NWAVES - 1) {
+      if (lane < T::K4S / 16)
+        load_to_lds(k4sb + (int64_t)j * (64 * D / 32) + 16 * lane, st + T::oK4S);
+      else if (lane < T::SC4)
+        load_to_lds(v4sb + (int64_t)j * (2 * D) + 16 * (lane - T::K4S / 16), st + T::oK4S);
+    }
+  };
   auto issue_loads = [&](uint8_t *st, int j, uint32_t h16) {
     if (h16 != head_bits) {
       for (int t = wave_u; t < T::G4; t += NWAVES) {
@@ -441,7 +485,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
           const int off = 1024 * t + 16 * lane, key = off / (D / 2), pch = (off % (D / 2)) / 16;
           src = k4b + (int64_t)j * (64 * D / 2) + key * (D / 2) + 16 * (pch ^ swz_k4<D>(key));
         } else {
-          src = v4b + (int64_t)j * (32 * D) + 1024 * (t - T::K4 / 1024) + 16 * lane;
+          const int o = 1024 * (t - T::K4 / 1024) + 16 * lane, ch = o / 32, pch = (o % 32) / 16;
+          src = v4b + (int64_t)j * (32 * D) + ch * 32 + 16 * (pch ^ swz_v4(ch));
         }
         load_to_lds(src, st + 1024 * t);
       }
@@ -501,18 +546,17 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     return nv;
   };
 
-  // Pass 0 normally finishes the work item.  If a phase-2 tile needed a
-  // shift beyond kMaxShift in some row, the workgroup makes pass 1 with every
-  // row's M preset to its true integer max (tracked in pass 0): no tile can
-  // then raise M, and pass 1 always finishes.
-  float mt_max = -INFINITY;
+  // Pass 0 normally finishes the work item.  If an FP4-only tile reached
+  // p > kMaxP in some row (a key far above every FP16-union block),
+  // the workgroup redoes the item as pass 1, whose FP4-only walk raises the
+  // running max as needed (the general tile body).
   for (int pass = 0; pass < 2; pass++) {
     float16v acc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[cb][r] = 0.0f;
-    float M = pass == 0 ? -INFINITY : mt_max, l_part = 0.0f;
+    float M = -INFINITY, l_part = 0.0f;
     bool overflow = false;
 
     // tile order: phase-1 tiles, the diagonal (causal), phase-2 tiles
@@ -532,9 +576,9 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
       const uint8_t *st = smem + par * T::STAGE;
       if (head_ok) {
         if ((h16_cur >> hl) & 1u)
-          tile_fp16<D, HPW, false>(st, qrow16, acc, M, l_part, mt_max, c, col, lh, qpos);
+          tile_fp16<D, HPW, false>(st, qrow16, acc, M, l_part, c, col, lh, qpos);
         else
-          tile_fp4<D, HPW, false>(st, qf4, qs4, acc, M, l_part, mt_max, c, col, lh, qpos);
+          tile_fp4<D, HPW, false>(st, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
       }
       wait_vmem();
       __syncthreads();
@@ -547,9 +591,9 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
       const uint8_t *st = smem + par * T::STAGE;
       if (head_ok) {
         if ((h16_cur >> hl) & 1u)
-          tile_fp16<D, HPW, true>(st, qrow16, acc, M, l_part, mt_max, c, col, lh, qpos);
+          tile_fp16<D, HPW, true>(st, qrow16, acc, M, l_part, c, col, lh, qpos);
         else
-          tile_fp4<D, HPW, true>(st, qf4, qs4, acc, M, l_part, mt_max, c, col, lh, qpos);
+          tile_fp4<D, HPW, true>(st, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
       }
       __syncthreads();
     }
@@ -557,32 +601,71 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     // 3-slot ring of FP4 stages (reusing the stage memory): while tile k is
     // in softmax/P.V, the QK MFMAs of tile k+1 are already issued and tile
     // k+2 is loading.  The loop is unrolled over the ring period so every LDS
-    // offset is a constant.
+    // offset is a constant.  The walk reads the complement of the FP16 union
+    // one 32-block word at a time, kept in a scalar register.
     {
-      int jc = next_tile(0, false);
-      int jn = (jc < nv) ? next_tile(jc + 1, false) : nv;
-      if (jc < nv) issue_loads(smem, jc, 0u);
-      if (jn < nv) issue_loads(smem + T::RING, jn, 0u);
+      int it_w = 0;
+      uint32_t it_bits = 0;  // unvisited FP4-only blocks of word it_w
+      auto it_load = [&](int w) {
+        it_w = w;
+        uint32_t m = (w < nw) ? ~(uint32_t)__builtin_amdgcn_readfirstlane(umask[w]) : 0u;
+        const int hi = jend - 32 * w;  // blocks of this word below jend
+        if (hi < 32) m &= hi > 0 ? ((1u << hi) - 1u) : 0u;
+        it_bits = m;
+      };
+      auto it_next = [&]() -> int {  // next FP4-only block in ascending order, else nv
+        while (it_bits == 0) {
+          if (it_w + 1 >= nw) return nv;
+          it_load(it_w + 1);
+        }
+        const int jj = 32 * it_w + __builtin_ctz(it_bits);
+        it_bits &= it_bits - 1;
+        return jj;
+      };
+      it_load(0);
+      int jc = it_next();
+      int jn = (jc < nv) ? it_next() : nv;
+      if (jc < nv) issue_fp4(smem, jc);
+      if (jn < nv) issue_fp4(smem + T::RING, jn);
       wait_vmem();
       __syncthreads();
       float16v sa[2], sb[2];
-      if (jc < nv && head_ok) fp4_qk<D, HPW>(smem, qf4, qs4, col, lh, sa);
+      if (pass == 0 && jc < nv && head_ok) {
+        fp4_qk<D, HPW>(smem, qf4, qs4, col, lh, sa);
+        // a row with no earlier tile takes its M from this first tile
+        const float lm = lane_max32(sa);
+        const float mt = ceilf(fmaxf(lm, other_half(lm)) * c);
+        M = (M == -INFINITY) ? mt : M;
+      }
       auto step = [&](const int cur, const int nxt, const int ldslot, float16v (&s_in)[2], float16v (&s_out)[2]) {
-        const int jnn = (jn < nv) ? next_tile(jn + 1, false) : nv;
-        if (jnn < nv) issue_loads(smem + ldslot * T::RING, jnn, 0u);
+        const int jnn = (jn < nv) ? it_next() : nv;
+        if (jnn < nv) issue_fp4(smem + ldslot * T::RING, jnn);
         if (head_ok) {
-          if (jn < nv) fp4_qk<D, HPW>(smem + nxt * T::RING, qf4, qs4, col, lh, s_out);
-          int4v va[CB];
-          int vs[CB];
+          // Issue order: every LDS operand read first (the next tile's K
+          // operands, this tile's V operands), then this tile's softmax with
+          // the next tile's QK MFMAs spread through it (in-order issue would
+          // otherwise hold the VALU work behind back-to-back MFMAs), then
+          // this tile's P.V MFMAs.  After the last tile the QK reads a stale
+          // slot; its result is never used.
+          int4v ka[2][D / 64], va[CB];
+          int ks[2][D / 64], vs[CB];
+          fp4_kops<D, HPW>(smem + nxt * T::RING, col, lh, ka, ks);
           fp4_vops<D, HPW>(smem + cur * T::RING, col, lh, va, vs);
-          fp4_fixed_rest<CB>(s_in, va, vs, acc, M, l_part, mt_max, overflow, c);
+          __builtin_amdgcn_sched_barrier(0);
+          fp4_qk_mfma<D>(ka, ks, qf4, qs4, s_out);
+          fp4_fixed_rest<CB>(s_in, va, vs, acc, M, l_part, overflow, c);
+#pragma unroll
+          for (int q = 0; q < 2 * (D / 64); q++) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (QK)
+          }
         }
         wait_vmem();
         __syncthreads();
         jc = jn;
         jn = jnn;
       };
-      while (jc < nv) {
+      while (pass == 0 && jc < nv) {
         step(0, 1, 2, sa, sb);
         if (jc >= nv) break;
         step(1, 2, 0, sb, sa);
@@ -594,6 +677,17 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
         step(1, 2, 0, sa, sb);
         if (jc >= nv) break;
         step(2, 0, 1, sb, sa);
+      }
+      // pass 1: the same walk, double-buffered, with the rescaling tile body
+      int p1 = 0;
+      while (pass == 1 && jc < nv) {
+        if (jn < nv) issue_fp4(smem + (p1 ^ 1) * T::RING, jn);
+        if (head_ok) tile_fp4<D, HPW, false>(smem + p1 * T::RING, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+        wait_vmem();
+        __syncthreads();
+        p1 ^= 1;
+        jc = jn;
+        jn = (jn < nv) ? it_next() : nv;
       }
     }
     if (pass == 0 && __syncthreads_or(overflow ? 1 : 0)) continue;
