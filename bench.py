@@ -170,6 +170,7 @@ def main():
     s = binding.make_shape(w.B, w.Hq, w.Hkv, w.N, w.d)
     ws = torch.empty(int(binding.lib().thrift_select_workspace_bytes(s)), dtype=torch.uint8, device=dev)
     out = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device=dev)
+    aws = torch.empty(binding.attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8, device=dev)
 
     def step(evs=None):
         if evs:
@@ -180,7 +181,7 @@ def main():
         binding.select(qz["q16"], qz["k16"], frac, True, workspace=ws, idx=idx, n16=n16)
         if evs:
             evs[2].record()
-        binding.attn_fwd(qz, idx, n16, True, out=out)
+        binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws)
         if evs:
             evs[3].record()
 

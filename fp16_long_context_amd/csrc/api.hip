@@ -92,10 +92,15 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
   return launch_select(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
 }
 
+size_t thrift_attn_workspace_bytes(const thrift_shape *s) {
+  if (check_shape(s) != THRIFT_OK) return 0;
+  return attn_workspace_bytes(s->B, s->Hq, s->N, s->d);
+}
+
 int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
                     const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
                     const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype, float *lse,
-                    void *stream) {
+                    void *workspace, size_t ws_bytes, void *stream) {
   int rc = check_shape(s);
   if (rc != THRIFT_OK) return rc;
   if (out_dtype != THRIFT_F16 && out_dtype != THRIFT_BF16 && out_dtype != THRIFT_F32) return THRIFT_EINVAL;
@@ -104,11 +109,13 @@ int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, cons
   for (const void *p : ptrs)
     if (!aligned_ok(p)) return THRIFT_EINVAL;
   if (lse && ((uintptr_t)lse & 15u)) return THRIFT_EINVAL;
+  if (!workspace || ws_bytes < thrift_attn_workspace_bytes(s)) return THRIFT_EWORKSPACE;
+  if (!aligned_ok(workspace)) return THRIFT_EINVAL;
   AttnArgs a;
   a.q16 = (const uint16_t *)q16; a.k16 = (const uint16_t *)k16; a.v16 = (const uint16_t *)v16;
   a.q4 = (const uint8_t *)q4; a.q4s = (const uint8_t *)q4s; a.k4 = (const uint8_t *)k4;
   a.k4s = (const uint8_t *)k4s; a.v4 = (const uint8_t *)v4; a.v4s = (const uint8_t *)v4s;
-  a.idx = idx; a.n16 = n16; a.out = out; a.lse = lse;
+  a.idx = idx; a.n16 = n16; a.out = out; a.lse = lse; a.ws = (float *)workspace;
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
   a.out_dtype = out_dtype;
   // score scale in log2 units, rounded once to fp32

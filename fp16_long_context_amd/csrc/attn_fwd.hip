@@ -6,11 +6,12 @@
 // Work decomposition (gfx950, wave64):
 //   * a workgroup owns one query block i (64 rows) of HPW query heads of one
 //     GQA group and walks the valid key blocks j = 0..n_valid-1 in ascending
-//     order -- the merge of the ascending FP16 and FP4 traversal lists;
-//   * per key block it stages the MXFP4 tile (K codes/scales, V codes/scales)
-//     when any of its heads has the block on its FP4 list and the FP16 tile
-//     (K and channel-major V) when any head has it on its FP16 list, so GQA
-//     heads share every K/V byte they read;
+//     order; for its own query rows every head computes block j either in
+//     FP16 (the block is on its FP16 list) or in FP4 (on its FP4 list);
+//   * per key block it stages the FP16 tile (K rows and channel-major V)
+//     when any head needs it and the MXFP4 tile (K codes/scales, V
+//     codes/scales) when any head needs that, so GQA heads share every K/V
+//     byte they read;
 //   * a wave owns 32 query rows of one head and computes S^T = K Q^T with
 //     32x32 MFMAs (FP16: v_mfma_f32_32x32x16_f16; FP4:
 //     v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 scales), then O^T += V^T P^T.
@@ -28,44 +29,49 @@
 // Online softmax.  The running max is an integer M in log2 units
 // (x = score * c, c = sm_scale * log2 e), so a change of M rescales the
 // accumulator and row sum by an exact power of two, which leaves the MXFP4
-// re-quantization of P (a per-group power-of-two scale) unchanged.  M is only
-// raised when a tile's max exceeds it by more than kLazy, so p stays below
-// 2^kLazy (fp16 P cannot overflow) and rescales are rare.
+// re-quantization of P (a per-group power-of-two scale) unchanged.  FP16
+// tiles (block 0 and the diagonal are always among them) raise M when their
+// max exceeds it by more than kLazy (fp16 P stays below 2^kLazy).  FP4 tiles
+// take p = 2^(x - M) against the M of the moment without raising it; their
+// group scales absorb any p above 1.  If some p exceeds kMaxP, or the result
+// is not finite, the work item is redone with a walk whose FP4 tiles raise M
+// as well.
 #include "thrift_internal.h"
 
 namespace thrift {
 
 constexpr float kLazy = 8.0f;
-// Largest p an FP4-only tile may reach against the running max (2^64).
-// With |v| <= 2^16 and at most 2^19 keys, acc stays below 2^(64 + 16 + 19)
-// = 2^99 and P's scale byte at most 127 + 64 - 2 = 189.
-constexpr float kMaxP = 0x1p64f;
+// Largest p an FP4 tile may take against the running max without raising
+// it: P's E8M0 scale byte stays at most 127 + 100 - 2, the row sum below
+// 2^(100 + 19); the accumulator is checked for overflow at the end.
+constexpr float kMaxP = 0x1p100f;
 
 template <int D, int HPW>
 struct Tile {
-  // FP4 stage
+  // FP4 tile, kept as two halves that are loaded and consumed at different
+  // steps: a K slot (K codes | K scale bytes) and a V slot (V codes | V
+  // scale bytes); the code regions are whole 1 KB groups.
   static constexpr int K4 = 64 * D / 2, K4S = 64 * D / 32, V4 = D * 32, V4S = D * 2;
-  static constexpr int FP4_BYTES = K4 + K4S + V4 + V4S;
-  // FP16 stage
+  static constexpr int KSLOT = K4 + K4S, VSLOT = V4 + V4S;
+  static constexpr int oK4 = 0, oK4S = K4;  // inside a K slot
+  static constexpr int oV4 = 0, oV4S = V4;  // inside a V slot
+  static constexpr int G4K = K4 / 1024, G4 = (K4 + V4) / 1024;  // 64-chunk groups of K codes, of K+V codes
+  // FP16 tile: K rows | channel-major V
   static constexpr int K16 = 64 * D * 2, V16 = D * 64 * 2;
   static constexpr int FP16_BYTES = K16 + V16;
-  static constexpr int STAGE = FP4_BYTES + FP16_BYTES;
-  // offsets inside a stage: codes first (whole 1 KB groups per region), then
-  // the K and V scale bytes
-  static constexpr int oK4 = 0, oV4 = K4, oK4S = K4 + V4, oV4S = K4 + V4 + K4S;
-  static constexpr int G4 = (K4 + V4) / 1024;    // 64-chunk groups of FP4 codes
-  static constexpr int SC4 = (K4S + V4S) / 16;   // 16-byte chunks of FP4 scales
-  static constexpr int G16 = (K16 + V16) / 1024; // 64-chunk groups of the FP16 stage
-  // the FP4-only walk uses a 3-slot ring of FP4 stages in the same memory
-  static constexpr int RING = FP4_BYTES;
-  static constexpr int oK16 = FP4_BYTES, oV16 = FP4_BYTES + K16;
-  // after the two stages: the workgroup's Q16 rows ([HPW*64][D] halves,
-  // 16-byte chunks XOR-swizzled by row) and the FP16-list bitmasks
-  static constexpr int oQ16 = 2 * STAGE;
+  static constexpr int oK16 = 0, oV16 = K16;
+  static constexpr int G16 = FP16_BYTES / 1024;  // 64-chunk groups of an FP16 tile
+  // Two slots of each kind: block j's FP16 tile and V half sit in slot j % 2;
+  // its K half too in the redo walk, while the main walk (FP4 QK one block
+  // ahead) loads the K half of block j + 2 into slot j % 2.
+  static constexpr int oSLOT16 = 0, oKSLOT = 2 * FP16_BYTES, oVSLOT = oKSLOT + 2 * KSLOT;
+  // then the workgroup's Q16 rows ([HPW*64][D] halves, 16-byte chunks
+  // XOR-swizzled by row) and the FP16-list bitmasks
+  static constexpr int oQ16 = oVSLOT + 2 * VSLOT;
   static constexpr int Q16_BYTES = HPW * 64 * D * 2;
   static constexpr int oMASK = oQ16 + Q16_BYTES;
-  static constexpr int oUMASK = oMASK + HPW * (kMaxBlocks / 32) * 4;  // union of the heads' FP16 lists
-  static constexpr int LDS = oUMASK + (kMaxBlocks / 32) * 4;
+  static constexpr int oIMASK = oMASK + HPW * (kMaxBlocks / 32) * 4;  // FP16 on every head
+  static constexpr int LDS = oIMASK + (kMaxBlocks / 32) * 4;
 };
 
 // LDS layouts of the staged tiles are XOR-swizzled in 16-byte chunks so that
@@ -98,6 +104,20 @@ __device__ __forceinline__ int permuted_key(int rho, int blk) {
 // 16 * lane (lds_wave_base must be the same for the whole wave).
 __device__ __forceinline__ void load_to_lds(const void *g, uint8_t *lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+// Buffer resource over a byte array: base p, no stride, no range clamp
+// (every offset the kernels form is inside the array).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, -1, 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff + soff (soff wave-uniform)
+// straight into LDS at lds_wave_base + 16 * lane.
+__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff,
+                                              uint8_t *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voff, soff,
+                                           0, 0);
 }
 
 // Wait until this wave's outstanding vector-memory loads (including the
@@ -222,14 +242,75 @@ __device__ __forceinline__ void fp4_vops(const uint8_t *st, const int col, const
   }
 }
 
+// LDS byte address (32-bit) of a pointer into the dynamic shared array, and
+// reads at such an address: a register plus a constant offset folds into
+// one ds_read.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+__device__ __forceinline__ int4v lds_read16(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) int4v *)(size_t)addr;
+}
+__device__ __forceinline__ int lds_read8(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) uint8_t *)(size_t)addr;
+}
+
+// Per-lane LDS addresses of the FP4 MFMA operand reads in K slot 0 and V
+// slot 0 (slot s adds s * KSLOT or s * VSLOT), so each read in the walk is
+// one of eight registers plus a constant.
+template <int D, int HPW>
+struct Fp4Offsets {
+  uint32_t k[2][D / 64];  // K codes of block blk, k-step kk
+  uint32_t ks[2];         // K scale bytes of block blk (+ 2 kk)
+  uint32_t v;             // V codes of channel block 0 (+ 1024 cb)
+  uint32_t vs;            // V scale bytes of channel block 0 (+ 64 cb)
+  __device__ __forceinline__ Fp4Offsets(const uint8_t *kslot0, const uint8_t *vslot0, const int col, const int lh) {
+    using T = Tile<D, HPW>;
+    const uint32_t kb = lds_addr(kslot0), vb = lds_addr(vslot0);
+#pragma unroll
+    for (int blk = 0; blk < 2; blk++) {
+      const int key = permuted_key(col, blk);
+#pragma unroll
+      for (int kk = 0; kk < D / 64; kk++)
+        k[blk][kk] = kb + T::oK4 + key * (D / 2) + 16 * ((2 * kk + lh) ^ swz_k4<D>(key));
+      ks[blk] = kb + T::oK4S + key * (D / 32) + lh;
+    }
+    // swz_v4 of channel 32 cb + col depends on col only
+    v = vb + T::oV4 + col * 32 + 16 * (lh ^ swz_v4(col));
+    vs = vb + T::oV4S + col * 2 + lh;
+  }
+};
+
+template <int D, int HPW>
+__device__ __forceinline__ void fp4_kops_at(const int slot_off, const Fp4Offsets<D, HPW> &fo,
+                                            int4v (&ka)[2][D / 64], int (&ks)[2][D / 64]) {
+#pragma unroll
+  for (int blk = 0; blk < 2; blk++)
+#pragma unroll
+    for (int kk = 0; kk < D / 64; kk++) {
+      ka[blk][kk] = lds_read16(fo.k[blk][kk] + slot_off);
+      ks[blk][kk] = lds_read8(fo.ks[blk] + slot_off + 2 * kk);
+    }
+}
+
+template <int D, int HPW>
+__device__ __forceinline__ void fp4_vops_at(const int slot_off, const Fp4Offsets<D, HPW> &fo, int4v (&va)[D / 32],
+                                            int (&vs)[D / 32]) {
+#pragma unroll
+  for (int cb = 0; cb < D / 32; cb++) {
+    va[cb] = lds_read16(fo.v + slot_off + 1024 * cb);
+    vs[cb] = lds_read8(fo.vs + slot_off + 64 * cb);
+  }
+}
+
 // FP4 tile, first half: S^T (masked on the diagonal) and the V operands
 // (read here so their LDS latency hides under the softmax).
 template <int D, int HPW, bool MASK>
-__device__ __forceinline__ void fp4_scores(const uint8_t *st, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
+__device__ __forceinline__ void fp4_scores(const uint8_t *kst, const uint8_t *vst, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
                                            const int col, const int lh, const int qpos, float16v (&s)[2],
                                            int4v (&va)[D / 32], int (&vs)[D / 32]) {
-  fp4_qk<D, HPW>(st, qf4, qs4, col, lh, s);
-  fp4_vops<D, HPW>(st, col, lh, va, vs);
+  fp4_qk<D, HPW>(kst, qf4, qs4, col, lh, s);
+  fp4_vops<D, HPW>(vst, col, lh, va, vs);
   if (MASK) {
 #pragma unroll
     for (int blk = 0; blk < 2; blk++)
@@ -241,11 +322,11 @@ __device__ __forceinline__ void fp4_scores(const uint8_t *st, const int4v (&qf4)
 
 // FP4 tile, second half: p (this lane's 32 values, one aligned 32-key group,
 // relative to the max the exponent used) re-quantized to MXFP4, and
-// O^T += V^T P^T.  `shift` is an extra power of two folded into P's E8M0
-// scale (the group's contribution is exactly 2^shift times its codes).
+// O^T += V^T P^T.
 template <int CB>
-__device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax, const int shift,
-                                       const int4v (&va)[CB], const int (&vs)[CB], float16v (&acc)[CB]) {
+__device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
+                                       const int4v (&va)[CB], const int (&vs)[CB], float16v (&acc)[CB],
+                                       const bool live = true) {
   const int psb = mx_scale_byte(amax);
   const float div = mx_scale_divisor(psb);
   uint32_t pw[4] = {0, 0, 0, 0};
@@ -256,41 +337,41 @@ __device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 2], s[blk][r0 + 3], div, 1);
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 4], s[blk][r0 + 5], div, 2);
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 6], s[blk][r0 + 7], div, 3);
+    pw[w] = live ? pw[w] : 0u;  // a skipped block adds exact zeros
   }
   int8v pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], 0, 0, 0, 0};
-  const int pscale = psb + shift;
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) {
     int8v a8 = {va[cb][0], va[cb][1], va[cb][2], va[cb][3], 0, 0, 0, 0};
-    acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, pb, acc[cb], 4, 4, 0, vs[cb], 0, pscale);
+    acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, pb, acc[cb], 4, 4, 0, vs[cb], 0, psb);
   }
 }
 
 // One FP4 tile (general walk): the running max may rise, rescaling acc.
 template <int D, int HPW, bool MASK>
-__device__ __forceinline__ void tile_fp4(const uint8_t *st, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
+__device__ __forceinline__ void tile_fp4(const uint8_t *kst, const uint8_t *vst, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
                                          float16v (&acc)[D / 32], float &M, float &l_part, const float c,
                                          const int col, const int lh, const int qpos) {
   constexpr int CB = D / 32;
   float16v s[2];
   int4v va[CB];
   int vs[CB];
-  fp4_scores<D, HPW, MASK>(st, qf4, qs4, col, lh, qpos, s, va, vs);
+  fp4_scores<D, HPW, MASK>(kst, vst, qf4, qs4, col, lh, qpos, s, va, vs);
   const float lane_max = softmax_step<CB, false>(s, acc, M, l_part, c, lh, qpos);
-  fp4_pv<CB>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, -M)), 0, va, vs, acc);
+  fp4_pv<CB>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, -M)), va, vs, acc);
 }
 
-// Softmax and P.V of one FP4-only tile whose scores s are already computed.
-// The running max M is final for this walk (it was set by the FP16-union
-// walk and the diagonal): p = 2^(s*c - M) is taken directly, so no step of
-// the exponentials waits on this tile's max.  P's group scale comes from the
-// largest p of the lane's 32-key group (the MXFP4 rule's amax, taken after
-// the exponentials); a group with amax above kMaxP (or infinite) sets
-// `overflow`, and the work item is then redone with the rescaling walk.
+// Softmax and P.V of one FP4 tile whose scores s are already computed,
+// against the running max M as it stands: p = 2^(s*c - M) is taken
+// directly, so no step of the exponentials waits on this tile's max, and the
+// accumulator is not rescaled.  p is summed into l_part unquantized; P's
+// group scale comes from the largest p of the lane's 32-key group (the MXFP4
+// rule's amax, taken after the exponentials).  A group with amax above kMaxP
+// (or not finite) sets `overflow`.
 template <int CB>
 __device__ __forceinline__ void fp4_fixed_rest(float16v (&s)[2], const int4v (&va)[CB], const int (&vs)[CB],
                                                float16v (&acc)[CB], const float M, float &l_part, bool &overflow,
-                                               const float c) {
+                                               const float c, const bool live) {
   const float negM = -M;
   float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
@@ -300,28 +381,40 @@ __device__ __forceinline__ void fp4_fixed_rest(float16v (&s)[2], const int4v (&v
     l0 += s[0][r];
     l1 += s[1][r];
   }
-  l_part += l0 + l1;
+  l_part += live ? l0 + l1 : 0.0f;
   const float amax = lane_max32(s);
-  overflow = overflow || !(amax <= kMaxP);
-  fp4_pv<CB>(s, amax, 0, va, vs, acc);
+  overflow = overflow || (live && !(amax <= kMaxP));
+  fp4_pv<CB>(s, amax, va, vs, acc, live);
 }
 
+// True if x is an infinity or a NaN (exponent field all ones); integer test,
+// so it holds whatever the compiler assumes about NaNs.
+__device__ __forceinline__ bool not_finite(float x) { return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u; }
+
 // One FP16 tile for one wave: S^T from FP16 K and Q, P rounded to fp16,
-// O^T += V^T P^T with FP16 V.  qrow16 points at this lane's Q16 row in LDS.
+// O^T += V^T P^T with FP16 V.  st16 is the tile's FP16 region (K rows, then
+// channel-major V); qrow16 points at this lane's Q16 row in LDS.
 template <int D, int HPW, bool MASK>
-__device__ __forceinline__ void tile_fp16(const uint8_t *st, const uint8_t *qrow16, float16v (&acc)[D / 32],
-                                          float &M, float &l_part, const float c, const int col, const int lh,
+__device__ __forceinline__ void tile_fp16(const uint8_t *st16, const uint8_t *qrow16, float16v (&acc)[D / 32],
+                                          float &M, float &l_part, const float c, const int col_in, const int lh,
                                           const int qpos) {
   using T = Tile<D, HPW>;
   constexpr int KS = D / 16, CB = D / 32, CPR = D / 8;  // k-steps, channel blocks, 16-byte chunks per row
+  // The per-lane operand addresses below are recomputed on every call: an
+  // empty asm makes the lane index opaque here, so they are not hoisted out
+  // of the walk loop (which would hold dozens of address registers across
+  // the hot FP4 steps).
+  int col_v = col_in;
+  asm volatile("" : "+v"(col_v));
+  const int col = col_v;
   float16v s[2];
 #pragma unroll
   for (int blk = 0; blk < 2; blk++)
 #pragma unroll
     for (int r = 0; r < 16; r++) s[blk][r] = 0.0f;
   const int key0 = permuted_key(col, 0), key1 = permuted_key(col, 1);
-  const uint8_t *k0 = st + T::oK16 + key0 * (2 * D);
-  const uint8_t *k1 = st + T::oK16 + key1 * (2 * D);
+  const uint8_t *k0 = st16 + T::oK16 + key0 * (2 * D);
+  const uint8_t *k1 = st16 + T::oK16 + key1 * (2 * D);
   const int sw0 = swz_k16<D>(key0), sw1 = swz_k16<D>(key1);
 #pragma unroll
   for (int kk = 0; kk < KS; kk += 2) {
@@ -346,7 +439,7 @@ __device__ __forceinline__ void tile_fp16(const uint8_t *st, const uint8_t *qrow
   for (int u = 0; u < 4; u++)
 #pragma unroll
     for (int t = 0; t < 8; t++) pb[u][t] = (_Float16)s[u >> 1][8 * (u & 1) + t];
-  const uint8_t *vt = st + T::oV16;
+  const uint8_t *vt = st16 + T::oV16;
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) {
     const int ch = 32 * cb + col;
@@ -359,49 +452,386 @@ __device__ __forceinline__ void tile_fp16(const uint8_t *st, const uint8_t *qrow
   }
 }
 
-template <int D, int HPW>
-__global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
-  using T = Tile<D, HPW>;
-  constexpr int NT = 128 * HPW;                  // threads
-  constexpr int KS4 = D / 64;                    // k-steps of the FP4 QK product
-  constexpr int CB = D / 32;                     // 32-channel blocks of O^T
-  constexpr int CPR = D / 8;                     // 16-byte chunks per Q16 row
+// Work item of one GQA workgroup: query block i of the HPW heads of chunk
+// `chunk` of GQA group g in batch b (longest causal rows first).
+struct WorkItem {
+  int i, b, g, chunk, nb, group, nv, nw;
+  __device__ __forceinline__ WorkItem(const AttnArgs &a, const int hpw) {
+    nb = a.N / 64;
+    group = a.Hq / a.Hkv;
+    const int chunks = (group + hpw - 1) / hpw;
+    const int per_i = a.B * a.Hkv * chunks;
+    const int wi = blockIdx.x / per_i;
+    int rem = blockIdx.x % per_i;
+    i = a.causal ? nb - 1 - wi : wi;
+    b = rem / (a.Hkv * chunks);
+    rem %= a.Hkv * chunks;
+    g = rem / chunks;
+    chunk = rem % chunks;
+    nv = a.causal ? i + 1 : nb;
+    nw = (nv + 31) / 32;
+  }
+};
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint32_t *mask = (uint32_t *)(smem + T::oMASK);  // [HPW][kMaxBlocks/32] FP16-list bits
+// K/V tile loads: direct copies into LDS (buffer_load ... lds; lane L of a
+// wave writes its 16 bytes at the wave-uniform LDS base + 16 L).  The array
+// base of this KV head sits in a scalar buffer resource, the block offset
+// j * (bytes per block) in a scalar register, and the per-lane offset inside
+// the block (with the chunk swizzle of the region) in a VGPR.  The waves of a
+// workgroup split a tile into whole 1 KB groups; the K and V scale bytes go
+// to the last two waves (to the only wave if there is one).  The caller
+// waits (vmcnt) before the barrier that publishes a tile.
+template <int D, int NWAVES>
+struct Loader {
+  using T = Tile<D, 1>;
+  static constexpr int NG4 = (T::G4 + NWAVES - 1) / NWAVES, NG16 = (T::G16 + NWAVES - 1) / NWAVES;
+  static constexpr int KSW = NWAVES >= 2 ? NWAVES - 2 : 0, VSW = NWAVES - 1;  // scale-byte waves
+  __amdgpu_buffer_rsrc_t rk4, rv4, rk4s, rv4s, rk16, rv16;
+  int wave_u, lane;
+  uint32_t goff4[NG4];
+  __device__ __forceinline__ Loader(const AttnArgs &a, const int b, const int hkv, const int wave_u_, const int lane_)
+      : wave_u(wave_u_), lane(lane_) {
+    const int nb = a.N / 64;
+    const int64_t kvh = (int64_t)b * a.Hkv + hkv;
+    rk4 = make_rsrc(a.k4 + kvh * a.N * (D / 2));
+    rv4 = make_rsrc(a.v4 + kvh * nb * (int64_t)(32 * D));
+    rk4s = make_rsrc(a.k4s + kvh * a.N * (D / 32));
+    rv4s = make_rsrc(a.v4s + kvh * nb * (int64_t)(2 * D));
+    rk16 = make_rsrc((const uint8_t *)a.k16 + kvh * a.N * (2 * D));
+    rv16 = make_rsrc((const uint8_t *)a.v16 + kvh * nb * (int64_t)(128 * D));
+#pragma unroll
+    for (int q = 0; q < NG4; q++) {
+      const int t = wave_u + q * NWAVES;
+      if (t < T::G4K) {
+        const int off = 1024 * t + 16 * lane, key = off / (D / 2), pch = (off % (D / 2)) / 16;
+        goff4[q] = key * (D / 2) + 16 * (pch ^ swz_k4<D>(key));
+      } else {
+        const int o = 1024 * (t - T::G4K) + 16 * lane, ch = o / 32, pch = (o % 32) / 16;
+        goff4[q] = ch * 32 + 16 * (pch ^ swz_v4(ch));
+      }
+    }
+  }
+  // K half of block j's FP4 tile into a K slot (codes move by 32 D bytes per
+  // block, scale bytes by 2 D)
+  __device__ __forceinline__ void k4(uint8_t *kst, const int j) const {
+#pragma unroll
+    for (int q = 0; q < NG4; q++) {
+      const int t = wave_u + q * NWAVES;
+      if (t < T::G4K) buffer_to_lds(rk4, goff4[q], j * (32 * D), kst + 1024 * t);
+    }
+    if (wave_u == KSW && lane < T::K4S / 16) buffer_to_lds(rk4s, 16 * lane, j * (2 * D), kst + T::oK4S);
+  }
+  // V half of block j's FP4 tile into a V slot
+  __device__ __forceinline__ void v4(uint8_t *vst, const int j) const {
+#pragma unroll
+    for (int q = 0; q < NG4; q++) {
+      const int t = wave_u + q * NWAVES;
+      if (t >= T::G4K && t < T::G4) buffer_to_lds(rv4, goff4[q], j * (32 * D), vst + 1024 * (t - T::G4K));
+    }
+    if (wave_u == VSW && lane < T::V4S / 16) buffer_to_lds(rv4s, 16 * lane, j * (2 * D), vst + T::oV4S);
+  }
+  // FP16 tile of block j into an FP16 slot (K16 and V16 move by 128 D bytes
+  // per block); the per-lane offsets are formed here.
+  __device__ __forceinline__ void fp16(uint8_t *st16, const int j) const {
+#pragma unroll
+    for (int q = 0; q < NG16; q++) {
+      const int t = wave_u + q * NWAVES;
+      if (t < T::K16 / 1024) {
+        const int off = 1024 * t + 16 * lane, key = off / (2 * D), pch = (off % (2 * D)) / 16;
+        buffer_to_lds(rk16, key * (2 * D) + 16 * (pch ^ swz_k16<D>(key)), j * (128 * D), st16 + 1024 * t);
+      } else if (t < T::G16) {
+        const int o = 1024 * (t - T::K16 / 1024) + 16 * lane, ch = o / 128, pch = (o % 128) / 16;
+        buffer_to_lds(rv16, ch * 128 + 16 * (pch ^ swz_v16(ch)), j * (128 * D), st16 + 1024 * t);
+      }
+    }
+  }
+};
 
-  const int nb = a.N / 64;
-  const int group = a.Hq / a.Hkv;
-  const int chunks = (group + HPW - 1) / HPW;
-  const int per_i = a.B * a.Hkv * chunks;
-  const int wi = blockIdx.x / per_i;
-  int rem = blockIdx.x % per_i;
-  const int i = a.causal ? nb - 1 - wi : wi;  // longest rows first
-  const int b = rem / (a.Hkv * chunks);
-  rem %= a.Hkv * chunks;
-  const int g = rem / chunks, chunk = rem % chunks;
-  const int nv = a.causal ? i + 1 : nb;
-  const int nw = (nv + 31) / 32;
+// Heads of the workgroup with block j on their FP16 list (wave-uniform).
+template <int HPW>
+__device__ __forceinline__ uint32_t fp16_heads(const uint32_t *mask, const int j, const uint32_t head_bits) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int h = 0; h < HPW; h++) m |= ((mask[h * (kMaxBlocks / 32) + (j >> 5)] >> (j & 31)) & 1u) << h;
+  return (uint32_t)__builtin_amdgcn_readfirstlane(m & head_bits);
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hl = wave >> 1, qhalf = wave & 1;
-  const int hgrp = chunk * HPW + hl;
-  const bool head_ok = hgrp < group;
-  const int hq = g * group + (head_ok ? hgrp : 0);
-  const int col = lane & 31, lh = lane >> 5;
-
-  // ---- FP16-list bitmask of each head of the workgroup
-  for (int w = tid; w < HPW * nw; w += NT) mask[(w / nw) * (kMaxBlocks / 32) + w % nw] = 0;
-  // ---- this wave's 32 query rows: Q16 into LDS (swizzled), Q4 into registers
-  const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf;
-  uint8_t *q16w = smem + T::oQ16 + (size_t)wave * 32 * D * 2;
+// One wave's 32 query rows of Q16 into LDS at q16w (row-major, 16-byte
+// chunks XOR-swizzled by row).
+template <int D>
+__device__ __forceinline__ void stage_q16(const AttnArgs &a, const int64_t qrow0, uint8_t *q16w, const int lane) {
+  constexpr int CPR = D / 8;
 #pragma unroll
   for (int it = 0; it < CPR / 2; it++) {  // 32 rows x CPR chunks over 64 lanes
     const int e = lane + 64 * it, row = e / CPR, ch = e % CPR;
     const int4v v = *(const int4v *)(a.q16 + (qrow0 + row) * D + 8 * ch);
     *(int4v *)(q16w + row * (2 * D) + 16 * (ch ^ (row & (CPR - 1)))) = v;
   }
+}
+
+// O = acc / l for this wave's 32 rows (lane: row col of the wave, channels
+// 8(r/4) + 4(lane/32) + r%4 of each 32-channel block), lse = (M + log2 l) ln 2.
+template <int D>
+__device__ __forceinline__ void store_rows(const AttnArgs &a, const float16v (&acc)[D / 32], const float M,
+                                           const float l_part, const int64_t qrow, const int lh) {
+  constexpr int CB = D / 32;
+  const float l = l_part + other_half(l_part);
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      const int ch = 32 * cb + 8 * q4 + 4 * lh;
+      float4v o = {acc[cb][4 * q4 + 0] * inv, acc[cb][4 * q4 + 1] * inv, acc[cb][4 * q4 + 2] * inv,
+                   acc[cb][4 * q4 + 3] * inv};
+      if (a.out_dtype == 2) {
+        *(float4v *)((float *)a.out + qrow * D + ch) = o;
+      } else if (a.out_dtype == 0) {
+        _Float16 *op = (_Float16 *)a.out + qrow * D + ch;
+        for (int e = 0; e < 4; e++) op[e] = (_Float16)o[e];
+      } else {
+        uint16_t *op = (uint16_t *)a.out + qrow * D + ch;
+        for (int e = 0; e < 4; e++) {
+          uint32_t u = __float_as_uint(o[e]);
+          u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even (finite values)
+          op[e] = (uint16_t)(u >> 16);
+        }
+      }
+    }
+  }
+  if (a.lse && lh == 0) a.lse[qrow] = (M + __log2f(l)) * 0.69314718055994530942f;
+}
+
+// Partial state of one wave's 32 rows after its FP16 blocks, handed from the
+// FP16 kernel to the FP4 kernel: per lane the D/2 accumulator values, the
+// running max M and the lane's part of the row sum, stored field-major
+// ([field][lane]) so both sides move whole 256-byte lines.
+template <int D>
+struct Partial {
+  static constexpr int FIELDS = D / 2 + 2;
+  static __device__ __forceinline__ float *at(float *ws, const int64_t wave_id) {
+    return ws + wave_id * (int64_t)(FIELDS * 64);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// FP16 kernel: one workgroup (two waves, 32 rows each) per query block i of
+// one head; walks the block's FP16 list (ascending, the diagonal last) with
+// the general online-softmax tile body and leaves the partial state in the
+// workspace.
+template <int D>
+struct Tile16 {
+  static constexpr int FP16_BYTES = Tile<D, 1>::FP16_BYTES;
+  static constexpr int oQ16 = 2 * FP16_BYTES;       // after two FP16 slots
+  static constexpr int LDS = oQ16 + 64 * D * 2;     // Q16 of the block's 64 rows
+};
+
+template <int D>
+__global__ __launch_bounds__(128) void attn_f16_kernel(AttnArgs a) {
+  using T = Tile<D, 1>;
+  constexpr int CB = D / 32;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int nb = a.N / 64, group = a.Hq / a.Hkv;
+  // Workgroups are dealt round-robin to the 8 XCDs (blockIdx % 8).  When the
+  // KV heads split evenly over them, every XCD gets whole KV heads: the
+  // group's query heads and neighbouring query blocks then share their FP16
+  // K/V tiles in that XCD's L2.  Longest causal rows first either way.
+  const int nkv = a.B * a.Hkv;
+  int wi, b, hq;
+  if (nkv % 8 == 0) {
+    const int x = blockIdx.x % 8, t = blockIdx.x / 8, kvb = nkv / 8;
+    const int kv = x + 8 * (t % kvb), t2 = t / kvb;
+    b = kv / a.Hkv;
+    hq = (kv % a.Hkv) * group + t2 % group;
+    wi = t2 / group;
+  } else {
+    const int per_i = a.B * a.Hq, bh0 = blockIdx.x % per_i;
+    wi = blockIdx.x / per_i;
+    b = bh0 / a.Hq;
+    hq = bh0 % a.Hq;
+  }
+  const int bh = b * a.Hq + hq;
+  const int i = a.causal ? nb - 1 - wi : wi;
+  const int nv = a.causal ? i + 1 : nb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, lh = lane >> 5;
+  const int qpos = 32 * wave_u + col;
+  const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * wave_u;
+  uint8_t *q16w = smem + Tile16<D>::oQ16 + (size_t)wave_u * 32 * D * 2;
+  stage_q16<D>(a, qrow0, q16w, lane);
+  const uint8_t *qrow16 = q16w + col * (2 * D);
+
+  const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
+  const int64_t roff = a.causal ? (int64_t)i * (i + 1) / 2 : (int64_t)i * nb;
+  const int32_t *l16 = a.idx + (int64_t)bh * per + roff;
+  const int cnt = min(max(a.n16[(int64_t)bh * nb + i], 0), nv);
+  // list entry e as a wave-uniform block index (-1 when outside [0, nv))
+  auto entry = [&](int e) {
+    const int j = __builtin_amdgcn_readfirstlane(l16[e]);
+    return ((unsigned)j < (unsigned)nv) ? j : -1;
+  };
+  const Loader<D, 2> ld(a, b, hq / group, wave_u, lane);
+
+  float16v acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[cb][r] = 0.0f;
+  float M = -INFINITY, l_part = 0.0f;
+  int jc = cnt > 0 ? entry(0) : -1;
+  if (jc >= 0) ld.fp16(smem, jc);
+  wait_vmem();
+  __syncthreads();
+  for (int e = 0; e < cnt; e++) {
+    const int jn = (e + 1 < cnt) ? entry(e + 1) : -1;
+    if (jn >= 0) ld.fp16(smem + ((e + 1) & 1) * T::FP16_BYTES, jn);
+    const uint8_t *st16 = smem + (e & 1) * T::FP16_BYTES;
+    if (a.causal && jc == i)
+      tile_fp16<D, 1, true>(st16, qrow16, acc, M, l_part, a.c, col, lh, qpos);
+    else if (jc >= 0)
+      tile_fp16<D, 1, false>(st16, qrow16, acc, M, l_part, a.c, col, lh, qpos);
+    wait_vmem();
+    __syncthreads();
+    jc = jn;
+  }
+  float *pw = Partial<D>::at(a.ws, ((int64_t)bh * nb + i) * 2 + wave_u);
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) pw[(16 * cb + r) * 64 + lane] = acc[cb][r];
+  pw[(D / 2) * 64 + lane] = M;
+  pw[(D / 2 + 1) * 64 + lane] = l_part;
+}
+
+// ---------------------------------------------------------------------------
+// Redo of a work item whose fixed-max FP4 walk overflowed: the full walk
+// over all blocks, FP16 and FP4, double-buffered (block j in slots j % 2),
+// with tile bodies that raise M whenever a block needs it; then the rows are
+// stored.  Kept out of line: it runs for few work items and its registers
+// must not weigh on the main walk.  Entered by every wave of the workgroup
+// (it has barriers); the FP16-list masks are already in LDS.
+template <int D, int HPW>
+__device__ __noinline__ void redo_item(const AttnArgs a_in, uint8_t *smem) {
+  using T = Tile<D, HPW>;
+  constexpr int KS4 = D / 64, CB = D / 32;
+  // Arguments of a call arrive in vector registers: make the (workgroup-
+  // uniform) arguments scalar again, word by word.
+  AttnArgs a;
+  {
+    static_assert(sizeof(AttnArgs) % 4 == 0, "AttnArgs is a sequence of 32-bit words");
+    uint32_t wv[sizeof(AttnArgs) / 4];
+    __builtin_memcpy(wv, &a_in, sizeof(AttnArgs));
+#pragma unroll
+    for (int e = 0; e < (int)(sizeof(AttnArgs) / 4); e++) wv[e] = (uint32_t)__builtin_amdgcn_readfirstlane((int)wv[e]);
+    __builtin_memcpy(&a, wv, sizeof(AttnArgs));
+  }
+  const WorkItem w(a, HPW);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = wave_u >> 1, qhalf = wave_u & 1;
+  const int hgrp = w.chunk * HPW + hl;
+  const bool head_ok = hgrp < w.group;
+  const int hq = w.g * w.group + (head_ok ? hgrp : 0);
+  const int col = lane & 31, lh = lane >> 5;
+  const uint32_t head_bits =
+      (w.chunk * HPW + HPW <= w.group) ? ((1u << HPW) - 1) : ((1u << (w.group - w.chunk * HPW)) - 1);
+  const uint32_t *mask = (const uint32_t *)(smem + T::oMASK);
+  const int64_t qrow0 = ((int64_t)w.b * a.Hq + hq) * a.N + 64 * (int64_t)w.i + 32 * qhalf;
   const int64_t qrow = qrow0 + col;
+  uint8_t *q16w = smem + T::oQ16 + (size_t)wave_u * 32 * D * 2;
+  stage_q16<D>(a, qrow0, q16w, lane);
+  const uint8_t *qrow16 = q16w + col * (2 * D);
+  const int qpos = 32 * qhalf + col;
+  int4v qf4[KS4];
+  int qs4[KS4];
+#pragma unroll
+  for (int kk = 0; kk < KS4; kk++) {
+    qf4[kk] = *(const int4v *)(a.q4 + qrow * (D / 2) + 32 * kk + 16 * lh);
+    qs4[kk] = a.q4s[qrow * (D / 32) + 2 * kk + lh];
+  }
+  const Loader<D, 2 * HPW> ld(a, w.b, w.g, wave_u, lane);
+  uint8_t *const slot16 = smem + T::oSLOT16, *const kslot = smem + T::oKSLOT, *const vslot = smem + T::oVSLOT;
+  const float c = a.c;
+  float16v acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[cb][r] = 0.0f;
+  float M = -INFINITY, l_part = 0.0f;
+  const int nv = w.nv;
+  uint32_t hc = fp16_heads<HPW>(mask, 0, head_bits);
+  if (hc != 0u) ld.fp16(slot16, 0);
+  if (hc != head_bits) {
+    ld.k4(kslot, 0);
+    ld.v4(vslot, 0);
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < nv; j++) {
+    const int sl = j & 1, sn = sl ^ 1;
+    const uint32_t hn = (j + 1 < nv) ? fp16_heads<HPW>(mask, j + 1, head_bits) : 0u;
+    if (j + 1 < nv) {
+      if (hn != 0u) ld.fp16(slot16 + sn * T::FP16_BYTES, j + 1);
+      if (hn != head_bits) {
+        ld.k4(kslot + sn * T::KSLOT, j + 1);
+        ld.v4(vslot + sn * T::VSLOT, j + 1);
+      }
+    }
+    if (head_ok) {
+      const bool fc = (hc >> hl) & 1u;
+      const uint8_t *s16 = slot16 + sl * T::FP16_BYTES, *ks4 = kslot + sl * T::KSLOT, *vs4 = vslot + sl * T::VSLOT;
+      if (a.causal && j == nv - 1) {
+        if (fc)
+          tile_fp16<D, HPW, true>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
+        else
+          tile_fp4<D, HPW, true>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+      } else {
+        if (fc)
+          tile_fp16<D, HPW, false>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
+        else
+          tile_fp4<D, HPW, false>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+    hc = hn;
+  }
+  if (head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
+}
+
+// ---------------------------------------------------------------------------
+// FP4 kernel: one workgroup per query block i of HPW heads of a GQA group
+// (a wave owns 32 rows of one head).  Each wave starts from the partial state
+// its head's FP16 blocks left in the workspace and walks, ascending, every
+// block below the diagonal that some head of the workgroup has on its FP4
+// list, with the FP4 QK product one block ahead.  The walk is the same for
+// all waves (K/V tiles are shared in LDS); a head skips a block of its own
+// FP16 list by adding neither p to l nor P.V to the accumulator.
+template <int D, int HPW>
+__global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
+  using T = Tile<D, HPW>;
+  constexpr int NT = 128 * HPW;                  // threads
+  constexpr int KS4 = D / 64;                    // k-steps of the FP4 QK product
+  constexpr int CB = D / 32;                     // 32-channel blocks of O^T
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint32_t *mask = (uint32_t *)(smem + T::oMASK);  // [HPW][kMaxBlocks/32] FP16-list bits
+  uint32_t *imask = (uint32_t *)(smem + T::oIMASK);  // blocks on every head's FP16 list
+
+  const WorkItem w(a, HPW);
+  const int i = w.i, b = w.b, g = w.g, chunk = w.chunk, nb = w.nb, group = w.group, nv = w.nv, nw = w.nw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = wave_u >> 1, qhalf = wave_u & 1;
+  const int hgrp = chunk * HPW + hl;
+  const bool head_ok = hgrp < group;
+  const int hq = g * group + (head_ok ? hgrp : 0);
+  const int col = lane & 31, lh = lane >> 5;
+
+  // ---- FP16-list bitmask of each head of the workgroup
+  for (int e = tid; e < HPW * nw; e += NT) mask[(e / nw) * (kMaxBlocks / 32) + e % nw] = 0;
+  const int64_t qrow = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf + col;
   int4v qf4[KS4];
   int qs4[KS4];
 #pragma unroll
@@ -425,302 +855,144 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   }
   __syncthreads();
   const uint32_t head_bits = (chunk * HPW + HPW <= group) ? ((1u << HPW) - 1) : ((1u << (group - chunk * HPW)) - 1);
-  auto fp16_heads = [&](int j) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int h = 0; h < HPW; h++) m |= ((mask[h * (kMaxBlocks / 32) + (j >> 5)] >> (j & 31)) & 1u) << h;
-    return (uint32_t)__builtin_amdgcn_readfirstlane(m & head_bits);
-  };
-
-  // ---- K/V tile loads: direct global -> LDS copies (global_load_lds_dwordx4;
-  // lane L of a wave writes its 16 bytes at the wave-uniform LDS base + 16 L).
-  // Each wave copies whole 1 KB groups of one region, so the region choice is
-  // scalar and the source address is a scalar base plus a per-lane offset
-  // (with the chunk swizzle of the region).  The caller waits (vmcnt) before
-  // the barrier that publishes the stage.
-  constexpr int NWAVES = 2 * HPW;
-  const int64_t kvh = (int64_t)b * a.Hkv + g;
-  const uint8_t *k4b = a.k4 + kvh * a.N * (D / 2), *k4sb = a.k4s + kvh * a.N * (D / 32);
-  const uint8_t *v4b = a.v4 + kvh * nb * (int64_t)(32 * D), *v4sb = a.v4s + kvh * nb * (int64_t)(2 * D);
-  const uint8_t *k16b = (const uint8_t *)a.k16 + kvh * a.N * (2 * D);
-  const uint8_t *v16b = (const uint8_t *)a.v16 + kvh * nb * (int64_t)(128 * D);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // FP4-only walk: this wave's code groups t = wave_u + g * NWAVES (< G4)
-  // have fixed per-lane offsets inside a tile; per tile only the scalar base
-  // moves (j times the array's per-block stride).
-  constexpr int NG4 = (T::G4 + NWAVES - 1) / NWAVES;
-  uint32_t goff[NG4];
-#pragma unroll
-  for (int g = 0; g < NG4; g++) {
-    const int t = wave_u + g * NWAVES;
-    if (t < T::K4 / 1024) {
-      const int off = 1024 * t + 16 * lane, key = off / (D / 2), pch = (off % (D / 2)) / 16;
-      goff[g] = key * (D / 2) + 16 * (pch ^ swz_k4<D>(key));
-    } else {
-      const int o = 1024 * (t - T::K4 / 1024) + 16 * lane, ch = o / 32, pch = (o % 32) / 16;
-      goff[g] = ch * 32 + 16 * (pch ^ swz_v4(ch));
-    }
-  }
-  auto issue_fp4 = [&](uint8_t *st, int j) {
-#pragma unroll
-    for (int g = 0; g < NG4; g++) {
-      const int t = wave_u + g * NWAVES;
-      if (t < T::G4) {
-        const uint8_t *base = (t < T::K4 / 1024) ? k4b + (int64_t)j * (64 * D / 2) : v4b + (int64_t)j * (32 * D);
-        load_to_lds(base + goff[g], st + 1024 * t);
-      }
-    }
-    if (wave_u == NWAVES - 1) {
-      if (lane < T::K4S / 16)
-        load_to_lds(k4sb + (int64_t)j * (64 * D / 32) + 16 * lane, st + T::oK4S);
-      else if (lane < T::SC4)
-        load_to_lds(v4sb + (int64_t)j * (2 * D) + 16 * (lane - T::K4S / 16), st + T::oK4S);
-    }
-  };
-  auto issue_loads = [&](uint8_t *st, int j, uint32_t h16) {
-    if (h16 != head_bits) {
-      for (int t = wave_u; t < T::G4; t += NWAVES) {
-        const uint8_t *src;
-        if (t < T::K4 / 1024) {
-          const int off = 1024 * t + 16 * lane, key = off / (D / 2), pch = (off % (D / 2)) / 16;
-          src = k4b + (int64_t)j * (64 * D / 2) + key * (D / 2) + 16 * (pch ^ swz_k4<D>(key));
-        } else {
-          const int o = 1024 * (t - T::K4 / 1024) + 16 * lane, ch = o / 32, pch = (o % 32) / 16;
-          src = v4b + (int64_t)j * (32 * D) + ch * 32 + 16 * (pch ^ swz_v4(ch));
-        }
-        load_to_lds(src, st + 1024 * t);
-      }
-      if (wave_u == NWAVES - 1 && lane < T::SC4) {
-        const uint8_t *src = lane < T::K4S / 16 ? k4sb + (int64_t)j * (64 * D / 32) + 16 * lane
-                                                : v4sb + (int64_t)j * (2 * D) + 16 * (lane - T::K4S / 16);
-        load_to_lds(src, st + T::oK4S);
-      }
-    }
-    if (h16 != 0) {
-      for (int t = wave_u; t < T::G16; t += NWAVES) {
-        const uint8_t *src;
-        if (t < T::K16 / 1024) {
-          const int off = 1024 * t + 16 * lane, key = off / (2 * D), pch = (off % (2 * D)) / 16;
-          src = k16b + (int64_t)j * (64 * 2 * D) + key * (2 * D) + 16 * (pch ^ swz_k16<D>(key));
-        } else {
-          const int o = 1024 * (t - T::K16 / 1024) + 16 * lane, ch = o / 128, pch = (o % 128) / 16;
-          src = v16b + (int64_t)j * (128 * D) + ch * 128 + 16 * (pch ^ swz_v16(ch));
-        }
-        load_to_lds(src, st + T::oK16 + 1024 * t);
-      }
-    }
-  };
-
-  const float c = a.c;
-  const int qpos = 32 * qhalf + col;  // query row inside the block
-  const uint8_t *qrow16 = q16w + col * (2 * D);
-
-  // ---- traversal.  Phase 1 walks the union of the heads' FP16 lists (all
-  // FP16 tiles, the first and the diagonal block), where the row max is
-  // almost always reached; phase 2 walks the blocks every head has on its
-  // FP4 list, with the accumulator left unscaled (fp4_fixed_rest).  Both
-  // walks are ascending and prefetch ahead of the tile being computed.
-  uint32_t *umask = (uint32_t *)(smem + T::oUMASK);
-  for (int w = tid; w < nw; w += NT) {
-    uint32_t u = 0;
+  for (int e = tid; e < nw; e += NT) {
+    uint32_t m = ~0u;
 #pragma unroll
     for (int h = 0; h < HPW; h++)
-      if ((head_bits >> h) & 1u) u |= mask[h * (kMaxBlocks / 32) + w];
-    umask[w] = u;
+      if ((head_bits >> h) & 1u) m &= mask[h * (kMaxBlocks / 32) + e];
+    imask[e] = m;
   }
-  __syncthreads();
-  // Causal rows end at the diagonal block, which takes the masked bodies and
-  // is handled on its own between the two walks (so neither walk's loop body
-  // branches on it).
-  const int jend = a.causal ? nv - 1 : nv;  // walks cover [0, jend)
-  auto next_tile = [&](int j, bool in16) -> int {  // smallest j' >= j of the walk's set below jend, else nv
-    for (int w = j >> 5; w < nw; w++) {
-      uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane(umask[w]);
-      if (!in16) m = ~m;
-      if (w == (j >> 5)) m &= ~0u << (j & 31);
-      if (m) {
-        const int jj = 32 * w + __builtin_ctz(m);
-        return jj < jend ? jj : nv;
-      }
-    }
-    return nv;
-  };
+  // this wave's head's FP16 bits, one word at a time
+  const uint32_t *own = mask + hl * (kMaxBlocks / 32);
 
-  // Pass 0 normally finishes the work item.  If an FP4-only tile reached
-  // p > kMaxP in some row (a key far above every FP16-union block),
-  // the workgroup redoes the item as pass 1, whose FP4-only walk raises the
-  // running max as needed (the general tile body).
-  for (int pass = 0; pass < 2; pass++) {
-    float16v acc[CB];
+  // ---- partial state of this wave's rows from the FP16 kernel
+  float16v acc[CB];
+  float M, l_part;
+  {
+    const int64_t bh = (int64_t)b * a.Hq + hq;
+    const float *pw = Partial<D>::at(a.ws, (bh * nb + i) * 2 + qhalf);
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) acc[cb][r] = 0.0f;
-    float M = -INFINITY, l_part = 0.0f;
-    bool overflow = false;
+      for (int r = 0; r < 16; r++) acc[cb][r] = pw[(16 * cb + r) * 64 + lane];
+    M = pw[(D / 2) * 64 + lane];
+    l_part = pw[(D / 2 + 1) * 64 + lane];
+  }
+  bool overflow = false;
+  __syncthreads();
 
-    // tile order: phase-1 tiles, the diagonal (causal), phase-2 tiles
-    int j = next_tile(0, true);
-    if (j >= nv) j = a.causal ? nv - 1 : nv;
-    uint32_t h16_cur = (j < nv) ? fp16_heads(j) : 0u;
-    int par = 0;
-    if (j < nv) issue_loads(smem, j, h16_cur);
+  const Loader<D, 2 * HPW> ld(a, b, g, wave_u, lane);
+  const float c = a.c;
+  const int qpos = 32 * qhalf + col;  // query row inside the block
+  uint8_t *const kslot = smem + T::oKSLOT, *const vslot = smem + T::oVSLOT;
+  // The walk covers [0, jend); causal rows end at the diagonal block, whose
+  // FP4 heads (if any) take the masked body after the walk.
+  const int jend = a.causal ? nv - 1 : nv;
+
+  // ---- the walk's blocks: not on every head's FP16 list, below jend; read
+  // one 32-block word at a time, kept in a scalar register
+  int it_w = 0;
+  uint32_t it_bits = 0;  // unvisited blocks of word it_w
+  auto it_load = [&](int wd) {
+    it_w = wd;
+    uint32_t m = (wd < nw) ? ~(uint32_t)__builtin_amdgcn_readfirstlane(imask[wd]) : 0u;
+    const int hi = jend - 32 * wd;  // blocks of this word below jend
+    if (hi < 32) m &= hi > 0 ? ((1u << hi) - 1u) : 0u;
+    it_bits = m;
+  };
+  auto it_next = [&]() -> int {  // next block of the walk in ascending order, else nv
+    while (it_bits == 0) {
+      if (it_w + 1 >= nw) return nv;
+      it_load(it_w + 1);
+    }
+    const int jj = 32 * it_w + __builtin_ctz(it_bits);
+    it_bits &= it_bits - 1;
+    return jj;
+  };
+  // is block j on this wave's head's FP4 list (wave-uniform)
+  auto own_fp4 = [&](int j) {
+    return head_ok && !(((uint32_t)__builtin_amdgcn_readfirstlane(own[j >> 5]) >> (j & 31)) & 1u);
+  };
+  it_load(0);
+  int j0 = it_next();                   // block of walk position m
+  int j1 = (j0 < nv) ? it_next() : nv;  // ... of position m + 1
+  if (j0 < nv) {
+    ld.k4(kslot, j0);
+    ld.v4(vslot, j0);
+  }
+  if (j1 < nv) ld.k4(kslot + T::KSLOT, j1);
+  wait_vmem();
+  __syncthreads();
+  float16v sa[2], sb[2];
+  if (j0 < nv) {
+    fp4_qk<D, HPW>(kslot, qf4, qs4, col, lh, sa);
+    // a row without FP16 blocks takes its M from this first tile
+    const float lm = lane_max32(sa);
+    const float mt = ceilf(fmaxf(lm, other_half(lm)) * c);
+    M = (M == -INFINITY) ? mt : M;
+  }
+  const Fp4Offsets<D, HPW> fo(kslot, vslot, col, lh);
+  // Step at walk position m (slots m % 2): loads the V half of position m+1
+  // and the K half of position m+2, issues the QK MFMAs of position m+1 and
+  // finishes position m (softmax and P.V).
+  auto step = [&](const int k, float16v (&s_in)[2], float16v (&s_out)[2]) {
+    const int kn = k ^ 1;
+    const int j2 = (j1 < nv) ? it_next() : nv;
+    if (j1 < nv) ld.v4(vslot + kn * T::VSLOT, j1);
+    if (j2 < nv) ld.k4(kslot + k * T::KSLOT, j2);
+    const bool live = own_fp4(j0);
+    // Issue order: every LDS operand read first (the next block's K
+    // operands, this block's V operands), then this block's softmax with the
+    // next block's QK MFMAs spread through it (in-order issue would otherwise
+    // hold the VALU work behind back-to-back MFMAs), then this block's P.V
+    // MFMAs.  After the last block the QK reads a stale slot; its result is
+    // never used.
+    int4v ka[2][D / 64], va[CB];
+    int ks[2][D / 64], vs[CB];
+    fp4_kops_at<D, HPW>(kn * T::KSLOT, fo, ka, ks);
+    fp4_vops_at<D, HPW>(k * T::VSLOT, fo, va, vs);
+    __builtin_amdgcn_sched_barrier(0);
+    fp4_qk_mfma<D>(ka, ks, qf4, qs4, s_out);
+    fp4_fixed_rest<CB>(s_in, va, vs, acc, M, l_part, overflow, c, live);
+#pragma unroll
+    for (int q = 0; q < 2 * (D / 64); q++) {
+      __builtin_amdgcn_sched_group_barrier(0x402, 20, 0);  // VALU (incl. transcendental)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (QK)
+    }
     wait_vmem();
     __syncthreads();
-    // phase 1 (below the diagonal)
-    while (j < jend) {
-      int jn = next_tile(j + 1, true);
-      if (jn >= nv) jn = a.causal ? nv - 1 : nv;
-      const uint32_t h16_next = (jn < nv) ? fp16_heads(jn) : 0u;
-      if (jn < nv) issue_loads(smem + (par ^ 1) * T::STAGE, jn, h16_next);
-      const uint8_t *st = smem + par * T::STAGE;
-      if (head_ok) {
-        if ((h16_cur >> hl) & 1u)
-          tile_fp16<D, HPW, false>(st, qrow16, acc, M, l_part, c, col, lh, qpos);
-        else
-          tile_fp4<D, HPW, false>(st, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
-      }
+    j0 = j1;
+    j1 = j2;
+  };
+  while (j0 < nv) {
+    step(0, sa, sb);
+    if (j0 >= nv) break;
+    step(1, sb, sa);
+  }
+  // the diagonal block (causal) for heads that have it on their FP4 list
+  if (a.causal) {
+    const uint32_t hd = fp16_heads<HPW>(mask, jend, head_bits);
+    if (hd != head_bits) {
+      ld.k4(kslot, jend);
+      ld.v4(vslot, jend);
       wait_vmem();
       __syncthreads();
-      par ^= 1;
-      j = jn;
-      h16_cur = h16_next;
+      if (head_ok && !((hd >> hl) & 1u))
+        tile_fp4<D, HPW, true>(kslot, vslot, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
     }
-    // the diagonal tile (causal)
-    if (j < nv) {
-      const uint8_t *st = smem + par * T::STAGE;
-      if (head_ok) {
-        if ((h16_cur >> hl) & 1u)
-          tile_fp16<D, HPW, true>(st, qrow16, acc, M, l_part, c, col, lh, qpos);
-        else
-          tile_fp4<D, HPW, true>(st, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
-      }
-      __syncthreads();
-    }
-    // Phase 2 (below the diagonal): every head computes these in FP4.  A
-    // 3-slot ring of FP4 stages (reusing the stage memory): while tile k is
-    // in softmax/P.V, the QK MFMAs of tile k+1 are already issued and tile
-    // k+2 is loading.  The loop is unrolled over the ring period so every LDS
-    // offset is a constant.  The walk reads the complement of the FP16 union
-    // one 32-block word at a time, kept in a scalar register.
-    {
-      int it_w = 0;
-      uint32_t it_bits = 0;  // unvisited FP4-only blocks of word it_w
-      auto it_load = [&](int w) {
-        it_w = w;
-        uint32_t m = (w < nw) ? ~(uint32_t)__builtin_amdgcn_readfirstlane(umask[w]) : 0u;
-        const int hi = jend - 32 * w;  // blocks of this word below jend
-        if (hi < 32) m &= hi > 0 ? ((1u << hi) - 1u) : 0u;
-        it_bits = m;
-      };
-      auto it_next = [&]() -> int {  // next FP4-only block in ascending order, else nv
-        while (it_bits == 0) {
-          if (it_w + 1 >= nw) return nv;
-          it_load(it_w + 1);
-        }
-        const int jj = 32 * it_w + __builtin_ctz(it_bits);
-        it_bits &= it_bits - 1;
-        return jj;
-      };
-      it_load(0);
-      int jc = it_next();
-      int jn = (jc < nv) ? it_next() : nv;
-      if (jc < nv) issue_fp4(smem, jc);
-      if (jn < nv) issue_fp4(smem + T::RING, jn);
-      wait_vmem();
-      __syncthreads();
-      float16v sa[2], sb[2];
-      if (pass == 0 && jc < nv && head_ok) {
-        fp4_qk<D, HPW>(smem, qf4, qs4, col, lh, sa);
-        // a row with no earlier tile takes its M from this first tile
-        const float lm = lane_max32(sa);
-        const float mt = ceilf(fmaxf(lm, other_half(lm)) * c);
-        M = (M == -INFINITY) ? mt : M;
-      }
-      auto step = [&](const int cur, const int nxt, const int ldslot, float16v (&s_in)[2], float16v (&s_out)[2]) {
-        const int jnn = (jn < nv) ? it_next() : nv;
-        if (jnn < nv) issue_fp4(smem + ldslot * T::RING, jnn);
-        if (head_ok) {
-          // Issue order: every LDS operand read first (the next tile's K
-          // operands, this tile's V operands), then this tile's softmax with
-          // the next tile's QK MFMAs spread through it (in-order issue would
-          // otherwise hold the VALU work behind back-to-back MFMAs), then
-          // this tile's P.V MFMAs.  After the last tile the QK reads a stale
-          // slot; its result is never used.
-          int4v ka[2][D / 64], va[CB];
-          int ks[2][D / 64], vs[CB];
-          fp4_kops<D, HPW>(smem + nxt * T::RING, col, lh, ka, ks);
-          fp4_vops<D, HPW>(smem + cur * T::RING, col, lh, va, vs);
-          __builtin_amdgcn_sched_barrier(0);
-          fp4_qk_mfma<D>(ka, ks, qf4, qs4, s_out);
-          fp4_fixed_rest<CB>(s_in, va, vs, acc, M, l_part, overflow, c);
+  }
+  // An FP4 group above kMaxP, or an accumulator or row sum that left the
+  // fp32 range, sends the work item to the redo walk.
+  bool bad = overflow || not_finite(l_part);
 #pragma unroll
-          for (int q = 0; q < 2 * (D / 64); q++) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);  // VALU
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (QK)
-          }
-        }
-        wait_vmem();
-        __syncthreads();
-        jc = jn;
-        jn = jnn;
-      };
-      while (pass == 0 && jc < nv) {
-        step(0, 1, 2, sa, sb);
-        if (jc >= nv) break;
-        step(1, 2, 0, sb, sa);
-        if (jc >= nv) break;
-        step(2, 0, 1, sa, sb);
-        if (jc >= nv) break;
-        step(0, 1, 2, sb, sa);
-        if (jc >= nv) break;
-        step(1, 2, 0, sa, sb);
-        if (jc >= nv) break;
-        step(2, 0, 1, sb, sa);
-      }
-      // pass 1: the same walk, double-buffered, with the rescaling tile body
-      int p1 = 0;
-      while (pass == 1 && jc < nv) {
-        if (jn < nv) issue_fp4(smem + (p1 ^ 1) * T::RING, jn);
-        if (head_ok) tile_fp4<D, HPW, false>(smem + p1 * T::RING, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
-        wait_vmem();
-        __syncthreads();
-        p1 ^= 1;
-        jc = jn;
-        jn = (jn < nv) ? it_next() : nv;
-      }
-    }
-    if (pass == 0 && __syncthreads_or(overflow ? 1 : 0)) continue;
-
-    // ---- epilogue: O = acc / l, lse = (M + log2 l) ln 2
-    if (!head_ok) return;
-    const float l = l_part + other_half(l_part);
-    const float inv = 1.0f / l;
+  for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-    for (int cb = 0; cb < CB; cb++) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        const int ch = 32 * cb + 8 * q4 + 4 * lh;  // rows 8(r/4) + 4(lane/32) + r%4 of block cb
-        float4v o = {acc[cb][4 * q4 + 0] * inv, acc[cb][4 * q4 + 1] * inv, acc[cb][4 * q4 + 2] * inv,
-                     acc[cb][4 * q4 + 3] * inv};
-        if (a.out_dtype == 2) {
-          *(float4v *)((float *)a.out + qrow * D + ch) = o;
-        } else if (a.out_dtype == 0) {
-          _Float16 *op = (_Float16 *)a.out + qrow * D + ch;
-          for (int e = 0; e < 4; e++) op[e] = (_Float16)o[e];
-        } else {
-          uint16_t *op = (uint16_t *)a.out + qrow * D + ch;
-          for (int e = 0; e < 4; e++) {
-            uint32_t u = __float_as_uint(o[e]);
-            u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest even (finite values)
-            op[e] = (uint16_t)(u >> 16);
-          }
-        }
-      }
-    }
-    if (a.lse && lh == 0) a.lse[qrow] = (M + __log2f(l)) * 0.69314718055994530942f;
+    for (int r = 0; r < 16; r++) bad = bad || not_finite(acc[cb][r]);
+  if (__syncthreads_or(bad ? 1 : 0)) {
+    redo_item<D, HPW>(a, smem);
     return;
   }
+  if (head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
 }
 
 template <int D, int HPW>
@@ -728,12 +1000,18 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
   using T = Tile<D, HPW>;
   const int group = a.Hq / a.Hkv;
   const int chunks = (group + HPW - 1) / HPW;
-  const size_t lds = (size_t)T::LDS;
-  hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const unsigned nb = (unsigned)(a.N / 64);
+  hipError_t e = hipFuncSetAttribute((const void *)attn_f16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     Tile16<D>::LDS);
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((int64_t)(a.N / 64) * a.B * a.Hkv * chunks);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW>), dim3(grid), dim3(128 * HPW), lds, st, a);
+  e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          T::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_f16_kernel<D>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(128), Tile16<D>::LDS, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW>), dim3(nb * (unsigned)(a.B * a.Hkv * chunks)), dim3(128 * HPW), T::LDS,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -748,6 +1026,10 @@ hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st) {
   if (hpw == 4) return launch_one<64, 4>(a, st);
   if (hpw == 2) return launch_one<64, 2>(a, st);
   return launch_one<64, 1>(a, st);
+}
+
+size_t attn_workspace_bytes(const int B, const int Hq, const int N, const int d) {
+  return (size_t)B * Hq * (N / 64) * 2 * 64 * (size_t)(d / 2 + 2) * sizeof(float);
 }
 
 }  // namespace thrift

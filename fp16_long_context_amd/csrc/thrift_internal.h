@@ -60,6 +60,7 @@ struct AttnArgs {
   const int32_t *idx, *n16;
   void *out;
   float *lse;
+  float *ws;  // partial state of every row after its FP16 blocks
   int B, Hq, Hkv, N, d, causal, out_dtype;
   float c;  // fl32(sm_scale * log2 e)
 };
@@ -67,5 +68,7 @@ struct AttnArgs {
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st);
+// bytes of the attention workspace (partial state of every query row)
+size_t attn_workspace_bytes(int B, int Hq, int N, int d);
 
 }  // namespace thrift

@@ -133,13 +133,21 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
  *   scores).
  * out [B,Hq,N,d] of out_dtype (THRIFT_F32, THRIFT_F16 or THRIFT_BF16);
  * lse [B,Hq,N] fp32, may be NULL.  idx/n16 must come from thrift_select with
- * the same shape (entries outside [0, n_valid) are not checked).
- * Errors: THRIFT_EINVAL (pointer, dtype).
+ * the same shape (list entries outside [0, n_valid) are skipped).
+ * workspace: device buffer of at least thrift_attn_workspace_bytes(s) bytes,
+ * 16-byte aligned, owned by the caller; on return it holds each row's
+ * partial softmax state after its FP16 blocks (no meaning for the caller).
+ * Calls sharing one workspace must not overlap in time.
+ * Errors: THRIFT_EINVAL (pointer, dtype, sm_scale), THRIFT_EWORKSPACE.
  */
 int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
                     const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
                     const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
-                    float *lse, void *stream);
+                    float *lse, void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of device workspace thrift_attn_fwd needs for shape s (0 if s is
+ * invalid): B * Hq * N/64 * 2 * 64 * (d/2 + 2) * 4. */
+size_t thrift_attn_workspace_bytes(const thrift_shape *s);
 
 /* Static string naming a status code. */
 const char *thrift_status_str(int status);

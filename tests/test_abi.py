@@ -53,9 +53,9 @@ def sel(L, s, frac=0.05, ptrs=None, ws=FAKE, wsb=1 << 40):
     return L.thrift_select(ctypes.byref(s), frac, *ptrs, ws, wsb, None)
 
 
-def attn(L, s, out_dtype=2, ptrs=None, lse=None, sm=0.0):
+def attn(L, s, out_dtype=2, ptrs=None, lse=None, sm=0.0, ws=FAKE, wsb=1 << 40):
     ptrs = ptrs or [FAKE] * 12
-    return L.thrift_attn_fwd(ctypes.byref(s), sm, *ptrs[:11], ptrs[11], out_dtype, lse, None)
+    return L.thrift_attn_fwd(ctypes.byref(s), sm, *ptrs[:11], ptrs[11], out_dtype, lse, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -69,14 +69,16 @@ def test_bad_shapes(L, kw, code):
     assert sel(L, s) == code
     assert attn(L, s) == code
     assert L.thrift_select_workspace_bytes(ctypes.byref(s)) == 0
+    assert L.thrift_attn_workspace_bytes(ctypes.byref(s)) == 0
     assert L.thrift_list_entries(ctypes.byref(s)) == 0
 
 
 def test_null_shape(L):
     assert L.thrift_quantize(None, 0, *[FAKE] * 12, None) == EINVAL
     assert L.thrift_select(None, 0.1, *[FAKE] * 4, FAKE, 1 << 40, None) == EINVAL
-    assert L.thrift_attn_fwd(None, 0.0, *[FAKE] * 12, 2, None, None) == EINVAL
+    assert L.thrift_attn_fwd(None, 0.0, *[FAKE] * 12, 2, None, FAKE, 1 << 40, None) == EINVAL
     assert L.thrift_select_workspace_bytes(None) == 0 and L.thrift_list_entries(None) == 0
+    assert L.thrift_attn_workspace_bytes(None) == 0
 
 
 @pytest.mark.parametrize("slot", range(12))
@@ -108,6 +110,12 @@ def test_workspace(L):
     assert sel(L, s, ws=None) == EWS
     assert sel(L, s, wsb=need - 1) == EWS
     assert sel(L, s, ws=ctypes.c_void_p(0x10004), wsb=need) == EINVAL
+    # attention: per row of every (b, head), two waves of 64 lanes x (d/2 + 2) fp32
+    need_a = L.thrift_attn_workspace_bytes(ctypes.byref(s))
+    assert need_a == 1 * 4 * 16 * 2 * 64 * (128 // 2 + 2) * 4
+    assert attn(L, s, ws=None) == EWS
+    assert attn(L, s, wsb=need_a - 1) == EWS
+    assert attn(L, s, ws=ctypes.c_void_p(0x10004), wsb=need_a) == EINVAL
 
 
 def test_list_entries(L):
