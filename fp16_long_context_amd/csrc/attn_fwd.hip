@@ -704,28 +704,48 @@ __global__ __launch_bounds__(128) void attn_f16_kernel(AttnArgs a) {
   pw[(D / 2 + 1) * 64 + lane] = l_part;
 }
 
+// FP16-list bitmask of each head of a GQA workgroup in LDS:
+// mask[h][j/32] bit j%32 set when block j is on head h's FP16 list.  Ends
+// with a barrier.
+template <int HPW>
+__device__ __forceinline__ void build_masks(const AttnArgs &a, const WorkItem &w, uint32_t *mask) {
+  constexpr int NT = 128 * HPW;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < HPW * w.nw; e += NT) mask[(e / w.nw) * (kMaxBlocks / 32) + e % w.nw] = 0;
+  __syncthreads();
+  const int64_t per = a.causal ? (int64_t)w.nb * (w.nb + 1) / 2 : (int64_t)w.nb * w.nb;
+  const int64_t roff = a.causal ? (int64_t)w.i * (w.i + 1) / 2 : (int64_t)w.i * w.nb;
+  for (int h = 0; h < HPW; h++) {
+    const int hg = w.chunk * HPW + h;
+    if (hg >= w.group) break;
+    const int64_t bh = (int64_t)w.b * a.Hq + w.g * w.group + hg;
+    const int cnt = a.n16[bh * w.nb + w.i];
+    const int32_t *l16 = a.idx + bh * per + roff;
+    for (int e = tid; e < cnt; e += NT) {
+      const int j = l16[e];
+      if ((unsigned)j < (unsigned)w.nv) atomicOr(&mask[h * (kMaxBlocks / 32) + (j >> 5)], 1u << (j & 31));
+    }
+  }
+  __syncthreads();
+}
+
+// Redo flag of F4 workgroup `wg` in the workspace (after the partial state).
+__device__ __forceinline__ int *redo_flags(const AttnArgs &a) {
+  return (int *)(a.ws + (size_t)a.B * a.Hq * (a.N / 64) * 2 * 64 * (a.d / 2 + 2));
+}
+
 // ---------------------------------------------------------------------------
-// Redo of a work item whose fixed-max FP4 walk overflowed: the full walk
-// over all blocks, FP16 and FP4, double-buffered (block j in slots j % 2),
-// with tile bodies that raise M whenever a block needs it; then the rows are
-// stored.  Kept out of line: it runs for few work items and its registers
-// must not weigh on the main walk.  Entered by every wave of the workgroup
-// (it has barriers); the FP16-list masks are already in LDS.
+// Redo kernel: for the work items whose fixed-max FP4 walk flagged an
+// overflow, the full walk over all blocks, FP16 and FP4, double-buffered
+// (block j in slots j % 2), with tile bodies that raise M whenever a block
+// needs it; then the rows are stored.  Same grid as the FP4 kernel; a
+// workgroup whose item was not flagged returns at once.
 template <int D, int HPW>
-__device__ __noinline__ void redo_item(const AttnArgs a_in, uint8_t *smem) {
+__global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
   using T = Tile<D, HPW>;
   constexpr int KS4 = D / 64, CB = D / 32;
-  // Arguments of a call arrive in vector registers: make the (workgroup-
-  // uniform) arguments scalar again, word by word.
-  AttnArgs a;
-  {
-    static_assert(sizeof(AttnArgs) % 4 == 0, "AttnArgs is a sequence of 32-bit words");
-    uint32_t wv[sizeof(AttnArgs) / 4];
-    __builtin_memcpy(wv, &a_in, sizeof(AttnArgs));
-#pragma unroll
-    for (int e = 0; e < (int)(sizeof(AttnArgs) / 4); e++) wv[e] = (uint32_t)__builtin_amdgcn_readfirstlane((int)wv[e]);
-    __builtin_memcpy(&a, wv, sizeof(AttnArgs));
-  }
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  if (redo_flags(a)[blockIdx.x] == 0) return;
   const WorkItem w(a, HPW);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -736,7 +756,8 @@ __device__ __noinline__ void redo_item(const AttnArgs a_in, uint8_t *smem) {
   const int col = lane & 31, lh = lane >> 5;
   const uint32_t head_bits =
       (w.chunk * HPW + HPW <= w.group) ? ((1u << HPW) - 1) : ((1u << (w.group - w.chunk * HPW)) - 1);
-  const uint32_t *mask = (const uint32_t *)(smem + T::oMASK);
+  uint32_t *mask = (uint32_t *)(smem + T::oMASK);
+  build_masks<HPW>(a, w, mask);
   const int64_t qrow0 = ((int64_t)w.b * a.Hq + hq) * a.N + 64 * (int64_t)w.i + 32 * qhalf;
   const int64_t qrow = qrow0 + col;
   uint8_t *q16w = smem + T::oQ16 + (size_t)wave_u * 32 * D * 2;
@@ -829,8 +850,6 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   const int hq = g * group + (head_ok ? hgrp : 0);
   const int col = lane & 31, lh = lane >> 5;
 
-  // ---- FP16-list bitmask of each head of the workgroup
-  for (int e = tid; e < HPW * nw; e += NT) mask[(e / nw) * (kMaxBlocks / 32) + e % nw] = 0;
   const int64_t qrow = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf + col;
   int4v qf4[KS4];
   int qs4[KS4];
@@ -839,21 +858,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     qf4[kk] = *(const int4v *)(a.q4 + qrow * (D / 2) + 32 * kk + 16 * lh);
     qs4[kk] = a.q4s[qrow * (D / 32) + 2 * kk + lh];
   }
-  __syncthreads();
-  const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
-  const int64_t roff = a.causal ? (int64_t)i * (i + 1) / 2 : (int64_t)i * nb;
-  for (int h = 0; h < HPW; h++) {
-    const int hg = chunk * HPW + h;
-    if (hg >= group) break;
-    const int64_t bh = (int64_t)b * a.Hq + g * group + hg;
-    const int cnt = a.n16[bh * nb + i];
-    const int32_t *l16 = a.idx + bh * per + roff;
-    for (int e = tid; e < cnt; e += NT) {
-      const int j = l16[e];
-      if ((unsigned)j < (unsigned)nv) atomicOr(&mask[h * (kMaxBlocks / 32) + (j >> 5)], 1u << (j & 31));
-    }
-  }
-  __syncthreads();
+  // ---- FP16-list bitmask of each head of the workgroup
+  build_masks<HPW>(a, w, mask);
   const uint32_t head_bits = (chunk * HPW + HPW <= group) ? ((1u << HPW) - 1) : ((1u << (group - chunk * HPW)) - 1);
   for (int e = tid; e < nw; e += NT) {
     uint32_t m = ~0u;
@@ -862,7 +868,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
       if ((head_bits >> h) & 1u) m &= mask[h * (kMaxBlocks / 32) + e];
     imask[e] = m;
   }
-  // this wave's head's FP16 bits, one word at a time
+  // this wave's head's FP16 bits
   const uint32_t *own = mask + hl * (kMaxBlocks / 32);
 
   // ---- partial state of this wave's rows from the FP16 kernel
@@ -893,29 +899,35 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   // one 32-block word at a time, kept in a scalar register
   int it_w = 0;
   uint32_t it_bits = 0;  // unvisited blocks of word it_w
+  uint32_t it_own = 0;   // this wave's head's FP16 bits of word it_w
   auto it_load = [&](int wd) {
     it_w = wd;
     uint32_t m = (wd < nw) ? ~(uint32_t)__builtin_amdgcn_readfirstlane(imask[wd]) : 0u;
     const int hi = jend - 32 * wd;  // blocks of this word below jend
     if (hi < 32) m &= hi > 0 ? ((1u << hi) - 1u) : 0u;
     it_bits = m;
+    it_own = (wd < nw) ? (uint32_t)__builtin_amdgcn_readfirstlane(own[wd]) : 0u;
   };
-  auto it_next = [&]() -> int {  // next block of the walk in ascending order, else nv
+  // Next block of the walk in ascending order (else nv), and whether this
+  // wave's head has it on its FP4 list (so the flag is known steps ahead).
+  uint32_t live_q = 0;  // FP4 flags of the blocks handed out, newest in bit 0
+  auto it_next = [&]() -> int {
     while (it_bits == 0) {
-      if (it_w + 1 >= nw) return nv;
+      if (it_w + 1 >= nw) {
+        live_q <<= 1;
+        return nv;
+      }
       it_load(it_w + 1);
     }
-    const int jj = 32 * it_w + __builtin_ctz(it_bits);
+    const int b = __builtin_ctz(it_bits);
     it_bits &= it_bits - 1;
-    return jj;
-  };
-  // is block j on this wave's head's FP4 list (wave-uniform)
-  auto own_fp4 = [&](int j) {
-    return head_ok && !(((uint32_t)__builtin_amdgcn_readfirstlane(own[j >> 5]) >> (j & 31)) & 1u);
+    live_q = (live_q << 1) | ((it_own >> b) & 1u ? 0u : 1u);
+    return 32 * it_w + b;
   };
   it_load(0);
   int j0 = it_next();                   // block of walk position m
   int j1 = (j0 < nv) ? it_next() : nv;  // ... of position m + 1
+  if (j0 >= nv) live_q <<= 1;
   if (j0 < nv) {
     ld.k4(kslot, j0);
     ld.v4(vslot, j0);
@@ -938,9 +950,10 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   auto step = [&](const int k, float16v (&s_in)[2], float16v (&s_out)[2]) {
     const int kn = k ^ 1;
     const int j2 = (j1 < nv) ? it_next() : nv;
+    if (j1 >= nv) live_q <<= 1;
     if (j1 < nv) ld.v4(vslot + kn * T::VSLOT, j1);
     if (j2 < nv) ld.k4(kslot + k * T::KSLOT, j2);
-    const bool live = own_fp4(j0);
+    const bool live = head_ok && ((live_q >> 2) & 1u);  // flag of j0 (two blocks behind j2)
     // Issue order: every LDS operand read first (the next block's K
     // operands, this block's V operands), then this block's softmax with the
     // next block's QK MFMAs spread through it (in-order issue would otherwise
@@ -982,17 +995,16 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     }
   }
   // An FP4 group above kMaxP, or an accumulator or row sum that left the
-  // fp32 range, sends the work item to the redo walk.
+  // fp32 range, leaves the work item to the redo kernel (flag in the
+  // workspace, written for every work item).
   bool bad = overflow || not_finite(l_part);
 #pragma unroll
   for (int cb = 0; cb < CB; cb++)
 #pragma unroll
     for (int r = 0; r < 16; r++) bad = bad || not_finite(acc[cb][r]);
-  if (__syncthreads_or(bad ? 1 : 0)) {
-    redo_item<D, HPW>(a, smem);
-    return;
-  }
-  if (head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
+  const int flagged = __syncthreads_or(bad ? 1 : 0);
+  if (tid == 0) redo_flags(a)[blockIdx.x] = flagged;
+  if (!flagged && head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
 }
 
 template <int D, int HPW>
@@ -1010,8 +1022,13 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((attn_f16_kernel<D>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(128), Tile16<D>::LDS, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW>), dim3(nb * (unsigned)(a.B * a.Hkv * chunks)), dim3(128 * HPW), T::LDS,
-                     st, a);
+  const dim3 grid4(nb * (unsigned)(a.B * a.Hkv * chunks));
+  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW>), grid4, dim3(128 * HPW), T::LDS, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW>, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_redo_kernel<D, HPW>), grid4, dim3(128 * HPW), T::LDS, st, a);
   return hipGetLastError();
 }
 
@@ -1029,7 +1046,9 @@ hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st) {
 }
 
 size_t attn_workspace_bytes(const int B, const int Hq, const int N, const int d) {
-  return (size_t)B * Hq * (N / 64) * 2 * 64 * (size_t)(d / 2 + 2) * sizeof(float);
+  // partial states, then one redo flag per FP4 workgroup (at most B * Hq * N/64)
+  return (size_t)B * Hq * (N / 64) * 2 * 64 * (size_t)(d / 2 + 2) * sizeof(float) +
+         (size_t)B * Hq * (N / 64) * sizeof(int);
 }
 
 }  // namespace thrift

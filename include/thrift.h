@@ -146,7 +146,7 @@ int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, cons
                     float *lse, void *workspace, size_t ws_bytes, void *stream);
 
 /* Bytes of device workspace thrift_attn_fwd needs for shape s (0 if s is
- * invalid): B * Hq * N/64 * 2 * 64 * (d/2 + 2) * 4. */
+ * invalid): B * Hq * N/64 * (2 * 64 * (d/2 + 2) + 1) * 4. */
 size_t thrift_attn_workspace_bytes(const thrift_shape *s);
 
 /* Static string naming a status code. */

@@ -110,9 +110,10 @@ def test_workspace(L):
     assert sel(L, s, ws=None) == EWS
     assert sel(L, s, wsb=need - 1) == EWS
     assert sel(L, s, ws=ctypes.c_void_p(0x10004), wsb=need) == EINVAL
-    # attention: per row of every (b, head), two waves of 64 lanes x (d/2 + 2) fp32
+    # attention: per query block of every (b, head), two waves of 64 lanes x
+    # (d/2 + 2) fp32 partial state, plus one int32 redo flag
     need_a = L.thrift_attn_workspace_bytes(ctypes.byref(s))
-    assert need_a == 1 * 4 * 16 * 2 * 64 * (128 // 2 + 2) * 4
+    assert need_a == 1 * 4 * 16 * (2 * 64 * (128 // 2 + 2) + 1) * 4
     assert attn(L, s, ws=None) == EWS
     assert attn(L, s, wsb=need_a - 1) == EWS
     assert attn(L, s, ws=ctypes.c_void_p(0x10004), wsb=need_a) == EINVAL

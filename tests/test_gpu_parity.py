@@ -148,3 +148,15 @@ def test_maximum_blocks():
     q, k, v = synth.random_qkv(1, 2, 1, 64 * 8192, 64, "fp16", seed=77)
     rows = np.array([0, 63, 64, 100000, 524287, 524288 + 524287, 524288 + 4097])
     run_case(q, k, v, 0.05, rows=rows, label="max-blocks")
+
+
+def test_redo_walk_on_overflow():
+    """A key far above every FP16 block of its rows sits in an FP4 block: the
+    fixed-max FP4 walk flags the work item (p would be ~2^190) and the redo
+    kernel recomputes it with the rescaling walk; the result must still
+    match the oracle."""
+    q, k, v = synth.random_qkv(1, 4, 1, 512, 128, "fp16", seed=77)
+    # key 200 (block 3, on no FP16 list at frac=0) aligned with query 450 of
+    # head 0 (block 7): score ~ 12 |q|^2 ~ 1500, x ~ 190 log2 units
+    k[0, 0, 200] = (12.0 * q[0, 0, 450].float()).to(q.dtype)
+    run_case(q, k, v, 0.0, label="redo walk")
