@@ -120,6 +120,25 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t
                                            0, 0);
 }
 
+// s_waitcnt immediate for vmcnt(n) alone (0 <= n < 64): the counter's low
+// four bits sit in bits 3:0, its high two in bits 15:14; expcnt (6:4) and
+// lgkmcnt (11:8) at their no-wait maxima.
+constexpr int vmcnt_imm(const int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+static_assert(vmcnt_imm(0) == 0x0F70 && vmcnt_imm(16) == 0x4F70, "vmcnt encoding");
+
+// Workgroup barrier after s_waitcnt vmcnt(n) lgkmcnt(0) (n < 64, a constant):
+// this wave's LDS accesses are done and at most its n newest vector-memory
+// loads are outstanding (direct-to-LDS copies that later steps wait for).
+// Unlike __syncthreads() it does not drain every outstanding load; the empty
+// asm statements keep the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void barrier_vmcnt() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N) & ~0x0F00);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait until this wave's outstanding vector-memory loads (including the
 // direct-to-LDS ones) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -615,63 +634,162 @@ struct Partial {
 };
 
 // ---------------------------------------------------------------------------
-// FP16 kernel: one workgroup (two waves, 32 rows each) per query block i of
-// one head; walks the block's FP16 list (ascending, the diagonal last) with
-// the general online-softmax tile body and leaves the partial state in the
-// workspace.
+// FP16 kernel: one workgroup (four waves) per query block i of one head;
+// walks the block's FP16 list (ascending, the diagonal last) and leaves the
+// partial state in the workspace.  Split over keys: wave w owns query rows
+// 32 (w & 1) + 0..31 and key half w >> 1 (keys 32 (w >> 1) + 0..31 of every
+// tile) with an online softmax of its own; the two key halves of a row are
+// merged at the end, so a tile needs no exchange between waves.
+#ifndef THRIFT_F16_SLOTS
+#define THRIFT_F16_SLOTS 2
+#endif
 template <int D>
 struct Tile16 {
   static constexpr int FP16_BYTES = Tile<D, 1>::FP16_BYTES;
-  static constexpr int oQ16 = 2 * FP16_BYTES;       // after two FP16 slots
-  static constexpr int LDS = oQ16 + 64 * D * 2;     // Q16 of the block's 64 rows
+  static constexpr int SLOTS = THRIFT_F16_SLOTS;      // ring of FP16 tiles: SLOTS - 1 loads in flight
+  static constexpr int oQ16 = SLOTS * FP16_BYTES;
+  static constexpr int LDS = oQ16 + 64 * D * 2;       // Q16 of the block's 64 rows
+  static_assert(Partial<D>::FIELDS * 64 * 4 * 2 <= SLOTS * FP16_BYTES, "merge buffer fits in the slots");
 };
 
+// Online-softmax step on one 32-query x 32-key score tile s (this lane:
+// query col, keys 16(r/8) + 8 lh + r%8 of the half): as softmax_step, for a
+// tile in which every row has at least one valid key.
+template <int CB, bool MASK>
+__device__ __forceinline__ void softmax_half(float16v &s, float16v (&acc)[CB], float &M, float &l_part, const float c,
+                                             const int key0, const int lh, const int qpos) {
+  if (MASK) {
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      if (key0 + 16 * (r >> 3) + 8 * lh + (r & 7) > qpos) s[r] = -INFINITY;
+  }
+  float m0 = fmaxf(s[0], s[1]), m1 = fmaxf(s[8], s[9]);
+#pragma unroll
+  for (int r = 2; r < 8; r += 2) {
+    m0 = fmaxf(fmaxf(m0, s[r]), s[r + 1]);
+    m1 = fmaxf(fmaxf(m1, s[8 + r]), s[9 + r]);
+  }
+  const float lane_max = fmaxf(m0, m1);
+  const float row_max = fmaxf(lane_max, other_half(lane_max));
+  const float mt = ceilf(row_max * c);  // integer candidate max (log2 units)
+  const bool raise = (mt > M + kLazy) || (M == -INFINITY);
+  if (__ballot(raise)) {  // wave-uniform; lanes that keep their max scale by 1
+    const float sc = raise ? ((M == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(M - mt))) : 1.0f;
+    M = raise ? mt : M;
+    l_part *= sc;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[cb][r] *= sc;
+  }
+  const float negM = -M;
+  float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 8; r++) {
+    s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, negM));
+    s[8 + r] = __builtin_amdgcn_exp2f(fmaf(s[8 + r], c, negM));
+    l0 += s[r];
+    l1 += s[8 + r];
+  }
+  l_part += l0 + l1;
+}
+
+// One 32-key half (keys 32 kh + 0..31) of an FP16 tile for one wave: S^T from
+// FP16 K and Q (K rows fed so that register r holds key 16(r/8) + 8 lh + r%8),
+// P rounded to fp16, O^T += V^T P^T with FP16 V.
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const uint8_t *qrow16, const int kh,
+                                               float16v (&acc)[D / 32], float &M, float &l_part, const float c,
+                                               const int col, const int lh, const int qpos) {
+  using T = Tile<D, 1>;
+  constexpr int KS = D / 16, CB = D / 32, CPR = D / 8;
+  // A-operand row rho reads key 16(rho/16) + 8((rho/4)%2) + 4((rho/8)%2) + rho%4
+  // of the half (bits 2 and 3 of rho swapped)
+  const int key = 32 * kh + (col & 0x13) + ((col & 4) << 1) + ((col & 8) >> 1);
+  const uint8_t *krow = st16 + T::oK16 + key * (2 * D);
+  const int sw = swz_k16<D>(key);
+  float16v s0, s1;
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    s0[r] = 0.0f;
+    s1[r] = 0.0f;
+  }
+#pragma unroll
+  for (int kk = 0; kk < KS; kk += 2) {
+    half8 qb[2], ka[2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int chunk = 2 * (kk + u) + lh;
+      qb[u] = __builtin_bit_cast(half8, *(const int4v *)(qrow16 + 16 * (chunk ^ (col & (CPR - 1)))));
+      ka[u] = __builtin_bit_cast(half8, *(const int4v *)(krow + 16 * (chunk ^ sw)));
+    }
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qb[0], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qb[1], s1, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; r++) s0[r] += s1[r];
+  softmax_half<CB, MASK>(s0, acc, M, l_part, c, 32 * kh, lh, qpos);
+  // P in fp16: MFMA u consumes keys 16u + 8 lh + 0..7 (registers 8u + 0..7)
+  half8 pb[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++)
+#pragma unroll
+    for (int t = 0; t < 8; t++) pb[u][t] = (_Float16)s0[8 * u + t];
+  const uint8_t *vt = st16 + T::oV16;
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+    const int ch = 32 * cb + col;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const half8 vf =
+          __builtin_bit_cast(half8, *(const int4v *)(vt + ch * 128 + 16 * ((4 * kh + 2 * u + lh) ^ swz_v16(ch))));
+      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb[u], acc[cb], 0, 0, 0);
+    }
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(128) void attn_f16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   using T = Tile<D, 1>;
   constexpr int CB = D / 32;
+  constexpr int F = Partial<D>::FIELDS;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int nb = a.N / 64, group = a.Hq / a.Hkv;
-  // Workgroups are dealt round-robin to the 8 XCDs (blockIdx % 8).  When the
-  // KV heads split evenly over them, every XCD gets whole KV heads: the
-  // group's query heads and neighbouring query blocks then share their FP16
-  // K/V tiles in that XCD's L2.  Longest causal rows first either way.
-  const int nkv = a.B * a.Hkv;
-  int wi, b, hq;
-  if (nkv % 8 == 0) {
-    const int x = blockIdx.x % 8, t = blockIdx.x / 8, kvb = nkv / 8;
-    const int kv = x + 8 * (t % kvb), t2 = t / kvb;
-    b = kv / a.Hkv;
-    hq = (kv % a.Hkv) * group + t2 % group;
-    wi = t2 / group;
-  } else {
-    const int per_i = a.B * a.Hq, bh0 = blockIdx.x % per_i;
-    wi = blockIdx.x / per_i;
-    b = bh0 / a.Hq;
-    hq = bh0 % a.Hq;
-  }
+  // KV-head-major order: the workgroups in flight at any time work on one
+  // or two KV heads, whose FP16 K/V (128 N d bytes each) then stays in the
+  // last-level cache while all their query heads and blocks read it.  Within
+  // a KV head, longest causal rows first.
+  const int kv = blockIdx.x / (nb * group), rem = blockIdx.x % (nb * group);
+  const int wi = rem / group;
+  const int b = kv / a.Hkv, hq = (kv % a.Hkv) * group + rem % group;
   const int bh = b * a.Hq + hq;
   const int i = a.causal ? nb - 1 - wi : wi;
   const int nv = a.causal ? i + 1 : nb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qhalf = wave_u & 1, kh = wave_u >> 1;
   const int col = lane & 31, lh = lane >> 5;
-  const int qpos = 32 * wave_u + col;
-  const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * wave_u;
-  uint8_t *q16w = smem + Tile16<D>::oQ16 + (size_t)wave_u * 32 * D * 2;
-  stage_q16<D>(a, qrow0, q16w, lane);
+  const int qpos = 32 * qhalf + col;
+  const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf;
+  uint8_t *q16w = smem + Tile16<D>::oQ16 + (size_t)qhalf * 32 * D * 2;
+  if (kh == 0) stage_q16<D>(a, qrow0, q16w, lane);
   const uint8_t *qrow16 = q16w + col * (2 * D);
 
   const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
   const int64_t roff = a.causal ? (int64_t)i * (i + 1) / 2 : (int64_t)i * nb;
-  const int32_t *l16 = a.idx + (int64_t)bh * per + roff;
-  const int cnt = min(max(a.n16[(int64_t)bh * nb + i], 0), nv);
-  // list entry e as a wave-uniform block index (-1 when outside [0, nv))
+  // the list is read through the constant address space: scalar loads,
+  // counted apart from the vector-memory loads of the tile ring
+  typedef const __attribute__((address_space(4))) int32_t cint;
+  cint *l16 = (cint *)(a.idx + (int64_t)bh * per + roff);
+  const int cnt = min(max(((cint *)a.n16)[(int64_t)bh * nb + i], 0), nv);
+  // list entry e as a wave-uniform block index; an entry outside [0, nv)
+  // (not produced by the selection) is clamped into it, so every access
+  // stays inside this KV head's arrays
   auto entry = [&](int e) {
-    const int j = __builtin_amdgcn_readfirstlane(l16[e]);
-    return ((unsigned)j < (unsigned)nv) ? j : -1;
+    const int j = l16[e];
+    return min(max(j, 0), nv - 1);
   };
-  const Loader<D, 2> ld(a, b, hq / group, wave_u, lane);
+  const Loader<D, 4> ld(a, b, hq / group, wave_u, lane);
 
   float16v acc[CB];
 #pragma unroll
@@ -679,29 +797,82 @@ __global__ __launch_bounds__(128) void attn_f16_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[cb][r] = 0.0f;
   float M = -INFINITY, l_part = 0.0f;
-  int jc = cnt > 0 ? entry(0) : -1;
-  if (jc >= 0) ld.fp16(smem, jc);
+  // Ring of SLOTS FP16 tiles: list entry e in slot e % SLOTS; the loads of
+  // entry e + SLOTS - 1 are issued while entry e is computed, and the wait
+  // at the end of an entry keeps the newer entries' loads in flight.
+  constexpr int R = Tile16<D>::SLOTS;
+  constexpr int LPT = Loader<D, 4>::NG16;  // load instructions per tile and wave
+  int jq[R];                                // blocks of entries e .. e + R - 1 (-1: none)
+#pragma unroll
+  for (int q = 0; q < R; q++) jq[q] = (q < cnt) ? entry(q) : -1;
+#pragma unroll
+  for (int q = 0; q < R - 1; q++)
+    if (jq[q] >= 0) ld.fp16(smem + q * T::FP16_BYTES, jq[q]);
   wait_vmem();
   __syncthreads();
-  for (int e = 0; e < cnt; e++) {
-    const int jn = (e + 1 < cnt) ? entry(e + 1) : -1;
-    if (jn >= 0) ld.fp16(smem + ((e + 1) & 1) * T::FP16_BYTES, jn);
-    const uint8_t *st16 = smem + (e & 1) * T::FP16_BYTES;
-    if (a.causal && jc == i)
-      tile_fp16<D, 1, true>(st16, qrow16, acc, M, l_part, a.c, col, lh, qpos);
-    else if (jc >= 0)
-      tile_fp16<D, 1, false>(st16, qrow16, acc, M, l_part, a.c, col, lh, qpos);
-    wait_vmem();
-    __syncthreads();
-    jc = jn;
+  // One step of the ring: finish entry e (its tile in slot e % R) with the
+  // loads of entry e + R - 1 in flight.
+  auto ring_step = [&](const int e, auto tile) {
+    const int jl = jq[R - 1];  // entry e + R - 1
+    if (jl >= 0) ld.fp16(smem + ((e + R - 1) % R) * T::FP16_BYTES, jl);
+    tile(smem + (e % R) * T::FP16_BYTES, jq[0]);
+    // entry e + 1 must have landed; entries e + 2 .. e + R - 1 may stay in flight
+    int inflight = 0;
+#pragma unroll
+    for (int q = 2; q < R; q++) inflight += jq[q] >= 0 ? 1 : 0;
+    if (R < 3 || inflight == 0)
+      barrier_vmcnt<0>();
+    else if (R < 4 || inflight == 1)
+      barrier_vmcnt<LPT>();
+    else
+      barrier_vmcnt<2 * LPT>();
+#pragma unroll
+    for (int q = 0; q < R - 1; q++) jq[q] = jq[q + 1];
+    jq[R - 1] = (e + R < cnt) ? entry(e + R) : -1;
+  };
+  // Entries before the last are never the diagonal (the list ascends and the
+  // diagonal block is the last valid one): one unmasked body, no branches.
+  for (int e = 0; e + 1 < cnt; e++)
+    ring_step(e, [&](const uint8_t *st16, int) {
+      tile_fp16_half<D, false>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+    });
+  if (cnt > 0)
+    ring_step(cnt - 1, [&](const uint8_t *st16, int jc) {
+      if (a.causal && jc == i) {
+        // the upper key half of the diagonal has no valid key for the lower rows
+        if (!(kh == 1 && qhalf == 0)) tile_fp16_half<D, true>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+      } else {
+        tile_fp16_half<D, false>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+      }
+    });
+  // Merge the two key halves of each row (lane by lane: the same lane of the
+  // two waves holds the same query and channels) through the slot memory,
+  // then the lower-half wave stores the row's partial state.
+  float *xch = (float *)smem + (size_t)qhalf * F * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) xch[(16 * cb + r) * 64 + lane] = acc[cb][r];
+    xch[(D / 2) * 64 + lane] = M;
+    xch[(D / 2 + 1) * 64 + lane] = l_part;
   }
-  float *pw = Partial<D>::at(a.ws, ((int64_t)bh * nb + i) * 2 + wave_u);
+  __syncthreads();
+  if (kh == 0) {
+    const float M1 = xch[(D / 2) * 64 + lane], l1 = xch[(D / 2 + 1) * 64 + lane];
+    const float Mn = fmaxf(M, M1);
+    // a half that saw no key has M = -inf and contributes nothing
+    const float s0 = (M == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(M - Mn));
+    const float s1 = (M1 == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(M1 - Mn));
+    float *pw = Partial<D>::at(a.ws, ((int64_t)bh * nb + i) * 2 + qhalf);
 #pragma unroll
-  for (int cb = 0; cb < CB; cb++)
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-    for (int r = 0; r < 16; r++) pw[(16 * cb + r) * 64 + lane] = acc[cb][r];
-  pw[(D / 2) * 64 + lane] = M;
-  pw[(D / 2 + 1) * 64 + lane] = l_part;
+      for (int r = 0; r < 16; r++)
+        pw[(16 * cb + r) * 64 + lane] = acc[cb][r] * s0 + xch[(16 * cb + r) * 64 + lane] * s1;
+    pw[(D / 2) * 64 + lane] = Mn;
+    pw[(D / 2 + 1) * 64 + lane] = l_part * s0 + l1 * s1;
+  }
 }
 
 // FP16-list bitmask of each head of a GQA workgroup in LDS:
@@ -1019,7 +1190,7 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
   e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           T::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_f16_kernel<D>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(128), Tile16<D>::LDS, st, a);
+  hipLaunchKernelGGL((attn_f16_kernel<D>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(256), Tile16<D>::LDS, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid4(nb * (unsigned)(a.B * a.Hkv * chunks));
