@@ -71,7 +71,11 @@ struct Tile {
   static constexpr int Q16_BYTES = HPW * 64 * D * 2;
   static constexpr int oMASK = oQ16 + Q16_BYTES;
   static constexpr int oIMASK = oMASK + HPW * (kMaxBlocks / 32) * 4;  // FP16 on every head
-  static constexpr int LDS = oIMASK + (kMaxBlocks / 32) * 4;
+  static constexpr int LDS = oIMASK + (kMaxBlocks / 32) * 4;             // redo kernel
+  // The FP4 kernel needs only the FP4 slots and the masks.
+  static constexpr int f4KSLOT = 0, f4VSLOT = 2 * KSLOT, f4MASK = f4VSLOT + 2 * VSLOT;
+  static constexpr int f4IMASK = f4MASK + HPW * (kMaxBlocks / 32) * 4;
+  static constexpr int F4_LDS = f4IMASK + (kMaxBlocks / 32) * 4;
 };
 
 // LDS layouts of the staged tiles are XOR-swizzled in 16-byte chunks so that
@@ -1008,8 +1012,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   constexpr int CB = D / 32;                     // 32-channel blocks of O^T
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint32_t *mask = (uint32_t *)(smem + T::oMASK);  // [HPW][kMaxBlocks/32] FP16-list bits
-  uint32_t *imask = (uint32_t *)(smem + T::oIMASK);  // blocks on every head's FP16 list
+  uint32_t *mask = (uint32_t *)(smem + T::f4MASK);  // [HPW][kMaxBlocks/32] FP16-list bits
+  uint32_t *imask = (uint32_t *)(smem + T::f4IMASK);  // blocks on every head's FP16 list
 
   const WorkItem w(a, HPW);
   const int i = w.i, b = w.b, g = w.g, chunk = w.chunk, nb = w.nb, group = w.group, nv = w.nv, nw = w.nw;
@@ -1061,7 +1065,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   const Loader<D, 2 * HPW> ld(a, b, g, wave_u, lane);
   const float c = a.c;
   const int qpos = 32 * qhalf + col;  // query row inside the block
-  uint8_t *const kslot = smem + T::oKSLOT, *const vslot = smem + T::oVSLOT;
+  uint8_t *const kslot = smem + T::f4KSLOT, *const vslot = smem + T::f4VSLOT;
   // The walk covers [0, jend); causal rows end at the diagonal block, whose
   // FP4 heads (if any) take the masked body after the walk.
   const int jend = a.causal ? nv - 1 : nv;
@@ -1188,13 +1192,13 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
                                      Tile16<D>::LDS);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          T::LDS);
+                          T::F4_LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_f16_kernel<D>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(256), Tile16<D>::LDS, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid4(nb * (unsigned)(a.B * a.Hkv * chunks));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW>), grid4, dim3(128 * HPW), T::LDS, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW>), grid4, dim3(128 * HPW), T::F4_LDS, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW>, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
@@ -1205,7 +1209,10 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st) {
   const int group = a.Hq / a.Hkv;
-  const int hpw = group >= 4 ? 4 : (group >= 2 ? 2 : 1);
+#ifndef THRIFT_F4_HPW_MAX
+#define THRIFT_F4_HPW_MAX 2
+#endif
+  const int hpw = (group >= 4 && THRIFT_F4_HPW_MAX >= 4) ? 4 : ((group >= 2 && THRIFT_F4_HPW_MAX >= 2) ? 2 : 1);
   if (a.d == 128) {
     if (hpw == 4) return launch_one<128, 4>(a, st);
     if (hpw == 2) return launch_one<128, 2>(a, st);
