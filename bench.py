@@ -8,12 +8,16 @@ Hq=32, Hkv=8, N=131072, d=128, causal, bf16 inputs, FP16 fraction 0.05).
 Prints one JSON line:
   value      attention flops of the step (4 d per causally valid query-key
              pair, F = 4 d B Hq N(N+1)/2) / measured step time, in TFLOP/s;
-  roofline   the fused attention kernel: achieved = F / its average launch
-             duration (HIP events on its stream), peak = the FP16/MXFP4 MFMA
-             roofline weighted by the flops in FP16 and FP4 tiles
+  roofline   the fused attention call thrift_attn_fwd, which is three
+             launches on one stream (attn_f16_kernel: FP16 blocks per head;
+             attn_fwd_kernel: FP4 blocks per GQA group, finishing each row;
+             attn_redo_kernel: exits at once unless an FP4 workgroup flagged
+             an overflow): achieved = F / the call's average duration (HIP
+             events on its stream), peak = the FP16/MXFP4 MFMA roofline
+             weighted by the flops in FP16 and FP4 tiles
              (F16 / 2516.6 TF/s + F4 / 10066 TF/s), traffic = HBM bytes per
-             launch from the committed rocprofv3 counter summary when it was
-             taken on the current kernel source, else null;
+             call (all three kernels) from the committed rocprofv3 counter
+             summary when it was taken on the current kernel source, else null;
   cpu_baseline  the CPU oracle's attention on a bounded row sample of the
              same workload, on this host's cores;
   kernels    quantize / select / attention times and algorithmic GB/s;
@@ -72,8 +76,8 @@ def select_bytes(w) -> float:
 
 
 def read_traffic():
-    """HBM bytes per launch of the fused kernel from the committed counter
-    summary, if it was measured on the current kernel source."""
+    """HBM bytes per attention call (its three kernels) from the committed
+    counter summary, if it was measured on the current kernel source."""
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     txt = open(TRAFFIC_SUMMARY).read()
@@ -230,7 +234,8 @@ def main():
                    "causal": True, "frac": frac, "in_dtype": w.dtype, "out_dtype": "f32"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "fp16_flop_share": round(F16 / F, 5), "kernel": "attn_fwd_kernel"},
+                     "fp16_flop_share": round(F16 / F, 5),
+                     "kernel": "thrift_attn_fwd = attn_f16_kernel + attn_fwd_kernel + attn_redo_kernel"},
         "kernels": {
             "quantize_ms": round(t_q, 4), "quantize_GBps": round(quantize_bytes(w) / (t_q * 1e-3) / 1e9, 1),
             "select_ms": round(t_s, 4), "select_GBps": round(select_bytes(w) / (t_s * 1e-3) / 1e9, 1),

@@ -3,18 +3,26 @@
 // query-key blocks are computed in FP16, the remaining ones in block-scaled
 // 4-bit, and both paths are merged by one online softmax into one output.
 //
-// Work decomposition (gfx950, wave64):
-//   * a workgroup owns one query block i (64 rows) of HPW query heads of one
-//     GQA group and walks the valid key blocks j = 0..n_valid-1 in ascending
-//     order; for its own query rows every head computes block j either in
-//     FP16 (the block is on its FP16 list) or in FP4 (on its FP4 list);
-//   * per key block it stages the FP16 tile (K rows and channel-major V)
-//     when any head needs it and the MXFP4 tile (K codes/scales, V
-//     codes/scales) when any head needs that, so GQA heads share every K/V
-//     byte they read;
-//   * a wave owns 32 query rows of one head and computes S^T = K Q^T with
-//     32x32 MFMAs (FP16: v_mfma_f32_32x32x16_f16; FP4:
-//     v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 scales), then O^T += V^T P^T.
+// Work decomposition (gfx950, wave64): three kernels on one stream.
+//   * attn_f16_kernel: one workgroup of 4 waves per (batch, query head,
+//     query block i) walks the FP16 list of that row block (block 0 and the
+//     diagonal block are always on it).  Each wave owns 32 query rows and
+//     one 32-key half of every 64-key tile, with its own online softmax; the
+//     two key halves are merged through LDS at the end and the partial state
+//     (unnormalised O^T, M, the lane's row-sum part) goes to the workspace.
+//   * attn_fwd_kernel: one workgroup per (batch, HPW query heads of one GQA
+//     group, query block i) starts from those partial states and walks, in
+//     ascending order, every block that is on the FP4 list of at least one
+//     of its heads, staging the block's MXFP4 K/V once for all of them.  A
+//     wave owns 32 query rows of one head and computes the blocks on its own
+//     head's FP4 list; the others are skipped.  It normalises and stores the
+//     rows, unless the overflow rule below flags the workgroup.
+//   * attn_redo_kernel: exits at once unless its work item was flagged, and
+//     then recomputes it from scratch with the general walk (every block in
+//     ascending order, FP16 or FP4 per head, M raised by either kind).
+// Every tile is S^T = K Q^T with 32x32 MFMAs (FP16: v_mfma_f32_32x32x16_f16;
+// FP4: v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 scales), then
+// O^T += V^T P^T.
 //
 // Lane layout.  In a 32x32 MFMA result, lane l holds column l%32 and rows
 // 8(r/4) + 4(l/32) + r%4 of accumulator register r.  K rows are fed to the
@@ -32,10 +40,10 @@
 // re-quantization of P (a per-group power-of-two scale) unchanged.  FP16
 // tiles (block 0 and the diagonal are always among them) raise M when their
 // max exceeds it by more than kLazy (fp16 P stays below 2^kLazy).  FP4 tiles
-// take p = 2^(x - M) against the M of the moment without raising it; their
-// group scales absorb any p above 1.  If some p exceeds kMaxP, or the result
-// is not finite, the work item is redone with a walk whose FP4 tiles raise M
-// as well.
+// take p = 2^(x - M) against the M left by the FP16 tiles without raising
+// it; their group scales absorb any p above 1.  If some p exceeds kMaxP, or
+// the result is not finite, the work item is redone with the general walk,
+// whose FP4 tiles raise M as well.
 #include "thrift_internal.h"
 
 namespace thrift {
@@ -61,9 +69,8 @@ struct Tile {
   static constexpr int FP16_BYTES = K16 + V16;
   static constexpr int oK16 = 0, oV16 = K16;
   static constexpr int G16 = FP16_BYTES / 1024;  // 64-chunk groups of an FP16 tile
-  // Two slots of each kind: block j's FP16 tile and V half sit in slot j % 2;
-  // its K half too in the redo walk, while the main walk (FP4 QK one block
-  // ahead) loads the K half of block j + 2 into slot j % 2.
+  // Two slots of each kind (redo walk): the FP16 tile, K half and V half of
+  // the block at walk position m sit in slot m % 2.
   static constexpr int oSLOT16 = 0, oKSLOT = 2 * FP16_BYTES, oVSLOT = oKSLOT + 2 * KSLOT;
   // then the workgroup's Q16 rows ([HPW*64][D] halves, 16-byte chunks
   // XOR-swizzled by row) and the FP16-list bitmasks
@@ -348,19 +355,20 @@ __device__ __forceinline__ void fp4_scores(const uint8_t *kst, const uint8_t *vs
 // O^T += V^T P^T.
 template <int CB>
 __device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
-                                       const int4v (&va)[CB], const int (&vs)[CB], float16v (&acc)[CB],
-                                       const bool live = true) {
+                                       const int4v (&va)[CB], const int (&vs)[CB], float16v (&acc)[CB]) {
   const int psb = mx_scale_byte(amax);
   const float div = mx_scale_divisor(psb);
-  uint32_t pw[4] = {0, 0, 0, 0};
+  uint32_t pw[4];
 #pragma unroll
   for (int w = 0; w < 4; w++) {
     const int blk = w >> 1, r0 = 8 * (w & 1);
+    // the four converts replace all four bytes; starting from s's own bits
+    // leaves the register allocator nothing to initialise
+    pw[w] = __float_as_uint(s[blk][r0]);
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 0], s[blk][r0 + 1], div, 0);
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 2], s[blk][r0 + 3], div, 1);
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 4], s[blk][r0 + 5], div, 2);
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 6], s[blk][r0 + 7], div, 3);
-    pw[w] = live ? pw[w] : 0u;  // a skipped block adds exact zeros
   }
   int8v pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], 0, 0, 0, 0};
 #pragma unroll
@@ -394,20 +402,23 @@ __device__ __forceinline__ void tile_fp4(const uint8_t *kst, const uint8_t *vst,
 template <int CB>
 __device__ __forceinline__ void fp4_fixed_rest(float16v (&s)[2], const int4v (&va)[CB], const int (&vs)[CB],
                                                float16v (&acc)[CB], const float M, float &l_part, bool &overflow,
-                                               const float c, const bool live) {
+                                               const float c) {
   const float negM = -M;
-  float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     s[0][r] = __builtin_amdgcn_exp2f(fmaf(s[0][r], c, negM));
     s[1][r] = __builtin_amdgcn_exp2f(fmaf(s[1][r], c, negM));
+  }
+  float l0 = s[0][0], l1 = s[1][0];
+#pragma unroll
+  for (int r = 1; r < 16; r++) {
     l0 += s[0][r];
     l1 += s[1][r];
   }
-  l_part += live ? l0 + l1 : 0.0f;
+  l_part += l0 + l1;
   const float amax = lane_max32(s);
-  overflow = overflow || (live && !(amax <= kMaxP));
-  fp4_pv<CB>(s, amax, va, vs, acc, live);
+  overflow = overflow || !(amax <= kMaxP);
+  fp4_pv<CB>(s, amax, va, vs, acc);
 }
 
 // True if x is an infinity or a NaN (exponent field all ones); integer test,
@@ -1100,62 +1111,58 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     return 32 * it_w + b;
   };
   it_load(0);
-  int j0 = it_next();                   // block of walk position m
-  int j1 = (j0 < nv) ? it_next() : nv;  // ... of position m + 1
-  if (j0 >= nv) live_q <<= 1;
+  int j0 = it_next();  // block of walk position m
   if (j0 < nv) {
     ld.k4(kslot, j0);
     ld.v4(vslot, j0);
   }
-  if (j1 < nv) ld.k4(kslot + T::KSLOT, j1);
   wait_vmem();
   __syncthreads();
-  float16v sa[2], sb[2];
   if (j0 < nv) {
-    fp4_qk<D, HPW>(kslot, qf4, qs4, col, lh, sa);
+    float16v s0[2];
+    fp4_qk<D, HPW>(kslot, qf4, qs4, col, lh, s0);
     // a row without FP16 blocks takes its M from this first tile
-    const float lm = lane_max32(sa);
+    const float lm = lane_max32(s0);
     const float mt = ceilf(fmaxf(lm, other_half(lm)) * c);
     M = (M == -INFINITY) ? mt : M;
   }
   const Fp4Offsets<D, HPW> fo(kslot, vslot, col, lh);
-  // Step at walk position m (slots m % 2): loads the V half of position m+1
-  // and the K half of position m+2, issues the QK MFMAs of position m+1 and
-  // finishes position m (softmax and P.V).
-  auto step = [&](const int k, float16v (&s_in)[2], float16v (&s_out)[2]) {
-    const int kn = k ^ 1;
-    const int j2 = (j1 < nv) ? it_next() : nv;
-    if (j1 >= nv) live_q <<= 1;
-    if (j1 < nv) ld.v4(vslot + kn * T::VSLOT, j1);
-    if (j2 < nv) ld.k4(kslot + k * T::KSLOT, j2);
-    const bool live = head_ok && ((live_q >> 2) & 1u);  // flag of j0 (two blocks behind j2)
-    // Issue order: every LDS operand read first (the next block's K
-    // operands, this block's V operands), then this block's softmax with the
-    // next block's QK MFMAs spread through it (in-order issue would otherwise
-    // hold the VALU work behind back-to-back MFMAs), then this block's P.V
-    // MFMAs.  After the last block the QK reads a stale slot; its result is
-    // never used.
-    int4v ka[2][D / 64], va[CB];
-    int ks[2][D / 64], vs[CB];
-    fp4_kops_at<D, HPW>(kn * T::KSLOT, fo, ka, ks);
-    fp4_vops_at<D, HPW>(k * T::VSLOT, fo, va, vs);
-    __builtin_amdgcn_sched_barrier(0);
-    fp4_qk_mfma<D>(ka, ks, qf4, qs4, s_out);
-    fp4_fixed_rest<CB>(s_in, va, vs, acc, M, l_part, overflow, c, live);
-#pragma unroll
-    for (int q = 0; q < 2 * (D / 64); q++) {
-      __builtin_amdgcn_sched_group_barrier(0x402, 20, 0);  // VALU (incl. transcendental)
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (QK)
+  // One FP4 block in slot k: QK, softmax against the fixed M, P.V.  The
+  // next block's QK is not started early: that would keep a second score
+  // tile live and cost the third wave per SIMD, which hides these latencies
+  // better.
+  auto block = [&](const int k) {
+    float16v s[2];
+    {
+      int4v ka[2][D / 64];
+      int ks[2][D / 64];
+      fp4_kops_at<D, HPW>(k * T::KSLOT, fo, ka, ks);
+      fp4_qk_mfma<D>(ka, ks, qf4, qs4, s);
     }
+    int4v va[CB];
+    int vs[CB];
+    fp4_vops_at<D, HPW>(k * T::VSLOT, fo, va, vs);
+    fp4_fixed_rest<CB>(s, va, vs, acc, M, l_part, overflow, c);
+  };
+  // Step at walk position m (slot m % 2): loads the K and V of position m+1
+  // into the other slot, then finishes position m if this wave's head has
+  // it on its FP4 list (a block walked only for the other head is skipped).
+  auto step = [&](const int k) {
+    const int kn = k ^ 1;
+    const int j1 = it_next();
+    if (j1 < nv) {
+      ld.k4(kslot + kn * T::KSLOT, j1);
+      ld.v4(vslot + kn * T::VSLOT, j1);
+    }
+    if (head_ok && ((live_q >> 1) & 1u)) block(k);  // flag of j0, one behind j1's
     wait_vmem();
     __syncthreads();
     j0 = j1;
-    j1 = j2;
   };
   while (j0 < nv) {
-    step(0, sa, sb);
+    step(0);
     if (j0 >= nv) break;
-    step(1, sb, sa);
+    step(1);
   }
   // the diagonal block (causal) for heads that have it on their FP4 list
   if (a.causal) {
