@@ -111,12 +111,6 @@ __device__ __forceinline__ int permuted_key(int rho, int blk) {
   return 32 * ((rho >> 2) & 1) + 16 * blk + 4 * (rho >> 3) + (rho & 3);
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds_wave_base +
-// 16 * lane (lds_wave_base must be the same for the whole wave).
-__device__ __forceinline__ void load_to_lds(const void *g, uint8_t *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
-}
-
 // Buffer resource over a byte array: base p, no stride, no range clamp
 // (every offset the kernels form is inside the array).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
@@ -124,11 +118,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
 }
 
 // 16 bytes per lane from buffer offset voff + soff (soff wave-uniform)
-// straight into LDS at lds_wave_base + 16 * lane.
+// straight into LDS at byte address lds_wave_base + 16 * lane
+// (lds_wave_base wave-uniform).  The LDS address is a plain 32-bit integer,
+// so forming it needs no generic-to-LDS pointer conversion.
 __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff,
-                                              uint8_t *lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voff, soff,
-                                           0, 0);
+                                              uint32_t lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(size_t)lds_wave_base, 16,
+                                           voff, soff, 0, 0);
 }
 
 // s_waitcnt immediate for vmcnt(n) alone (0 <= n < 64): the counter's low
@@ -545,9 +541,10 @@ struct Loader {
       }
     }
   }
-  // K half of block j's FP4 tile into a K slot (codes move by 32 D bytes per
-  // block, scale bytes by 2 D)
-  __device__ __forceinline__ void k4(uint8_t *kst, const int j) const {
+  // K half of block j's FP4 tile into the K slot at LDS address kst (codes
+  // move by 32 D bytes per block, scale bytes by 2 D)
+  __device__ __forceinline__ void k4(const uint32_t kst, const int j) const {
+    __builtin_assume(wave_u >= 0 && wave_u < NWAVES);
 #pragma unroll
     for (int q = 0; q < NG4; q++) {
       const int t = wave_u + q * NWAVES;
@@ -555,8 +552,9 @@ struct Loader {
     }
     if (wave_u == KSW && lane < T::K4S / 16) buffer_to_lds(rk4s, 16 * lane, j * (2 * D), kst + T::oK4S);
   }
-  // V half of block j's FP4 tile into a V slot
-  __device__ __forceinline__ void v4(uint8_t *vst, const int j) const {
+  // V half of block j's FP4 tile into the V slot at LDS address vst
+  __device__ __forceinline__ void v4(const uint32_t vst, const int j) const {
+    __builtin_assume(wave_u >= 0 && wave_u < NWAVES);
 #pragma unroll
     for (int q = 0; q < NG4; q++) {
       const int t = wave_u + q * NWAVES;
@@ -564,9 +562,10 @@ struct Loader {
     }
     if (wave_u == VSW && lane < T::V4S / 16) buffer_to_lds(rv4s, 16 * lane, j * (2 * D), vst + T::oV4S);
   }
-  // FP16 tile of block j into an FP16 slot (K16 and V16 move by 128 D bytes
-  // per block); the per-lane offsets are formed here.
-  __device__ __forceinline__ void fp16(uint8_t *st16, const int j) const {
+  // FP16 tile of block j into the FP16 slot at LDS address st16 (K16 and
+  // V16 move by 128 D bytes per block); the per-lane offsets are formed here.
+  __device__ __forceinline__ void fp16(const uint32_t st16, const int j) const {
+    __builtin_assume(wave_u >= 0 && wave_u < NWAVES);
 #pragma unroll
     for (int q = 0; q < NG16; q++) {
       const int t = wave_u + q * NWAVES;
@@ -822,14 +821,14 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   for (int q = 0; q < R; q++) jq[q] = (q < cnt) ? entry(q) : -1;
 #pragma unroll
   for (int q = 0; q < R - 1; q++)
-    if (jq[q] >= 0) ld.fp16(smem + q * T::FP16_BYTES, jq[q]);
+    if (jq[q] >= 0) ld.fp16(lds_addr(smem) + q * T::FP16_BYTES, jq[q]);
   wait_vmem();
   __syncthreads();
   // One step of the ring: finish entry e (its tile in slot e % R) with the
   // loads of entry e + R - 1 in flight.
   auto ring_step = [&](const int e, auto tile) {
     const int jl = jq[R - 1];  // entry e + R - 1
-    if (jl >= 0) ld.fp16(smem + ((e + R - 1) % R) * T::FP16_BYTES, jl);
+    if (jl >= 0) ld.fp16(lds_addr(smem) + ((e + R - 1) % R) * T::FP16_BYTES, jl);
     tile(smem + (e % R) * T::FP16_BYTES, jq[0]);
     // entry e + 1 must have landed; entries e + 2 .. e + R - 1 may stay in flight
     int inflight = 0;
@@ -968,10 +967,11 @@ __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
   float M = -INFINITY, l_part = 0.0f;
   const int nv = w.nv;
   uint32_t hc = fp16_heads<HPW>(mask, 0, head_bits);
-  if (hc != 0u) ld.fp16(slot16, 0);
+  const uint32_t slot16_a = lds_addr(slot16), kslot_a = lds_addr(kslot), vslot_a = lds_addr(vslot);
+  if (hc != 0u) ld.fp16(slot16_a, 0);
   if (hc != head_bits) {
-    ld.k4(kslot, 0);
-    ld.v4(vslot, 0);
+    ld.k4(kslot_a, 0);
+    ld.v4(vslot_a, 0);
   }
   wait_vmem();
   __syncthreads();
@@ -979,10 +979,10 @@ __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
     const int sl = j & 1, sn = sl ^ 1;
     const uint32_t hn = (j + 1 < nv) ? fp16_heads<HPW>(mask, j + 1, head_bits) : 0u;
     if (j + 1 < nv) {
-      if (hn != 0u) ld.fp16(slot16 + sn * T::FP16_BYTES, j + 1);
+      if (hn != 0u) ld.fp16(slot16_a + sn * T::FP16_BYTES, j + 1);
       if (hn != head_bits) {
-        ld.k4(kslot + sn * T::KSLOT, j + 1);
-        ld.v4(vslot + sn * T::VSLOT, j + 1);
+        ld.k4(kslot_a + sn * T::KSLOT, j + 1);
+        ld.v4(vslot_a + sn * T::VSLOT, j + 1);
       }
     }
     if (head_ok) {
@@ -1077,6 +1077,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   const float c = a.c;
   const int qpos = 32 * qhalf + col;  // query row inside the block
   uint8_t *const kslot = smem + T::f4KSLOT, *const vslot = smem + T::f4VSLOT;
+  const uint32_t kslot_a = lds_addr(smem) + T::f4KSLOT, vslot_a = lds_addr(smem) + T::f4VSLOT;
   // The walk covers [0, jend); causal rows end at the diagonal block, whose
   // FP4 heads (if any) take the masked body after the walk.
   const int jend = a.causal ? nv - 1 : nv;
@@ -1113,8 +1114,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   it_load(0);
   int j0 = it_next();  // block of walk position m
   if (j0 < nv) {
-    ld.k4(kslot, j0);
-    ld.v4(vslot, j0);
+    ld.k4(kslot_a, j0);
+    ld.v4(vslot_a, j0);
   }
   wait_vmem();
   __syncthreads();
@@ -1151,8 +1152,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     const int kn = k ^ 1;
     const int j1 = it_next();
     if (j1 < nv) {
-      ld.k4(kslot + kn * T::KSLOT, j1);
-      ld.v4(vslot + kn * T::VSLOT, j1);
+      ld.k4(kslot_a + kn * T::KSLOT, j1);
+      ld.v4(vslot_a + kn * T::VSLOT, j1);
     }
     if (head_ok && ((live_q >> 1) & 1u)) block(k);  // flag of j0, one behind j1's
     wait_vmem();
@@ -1168,8 +1169,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   if (a.causal) {
     const uint32_t hd = fp16_heads<HPW>(mask, jend, head_bits);
     if (hd != head_bits) {
-      ld.k4(kslot, jend);
-      ld.v4(vslot, jend);
+      ld.k4(kslot_a, jend);
+      ld.v4(vslot_a, jend);
       wait_vmem();
       __syncthreads();
       if (head_ok && !((hd >> hl) & 1u))
