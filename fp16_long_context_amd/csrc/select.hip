@@ -51,22 +51,34 @@ __device__ __forceinline__ uint64_t order_key(double s) {
 
 constexpr int kSelThreads = 256;
 
-// Exclusive prefix sum of one value per thread over the block; also returns
-// the total.  `buf` holds kSelThreads ints.
-__device__ int block_exclusive_scan(int v, int *buf, int &total) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    int add = (t >= off) ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+// Inclusive prefix sum of one value per lane over the wave (64 lanes).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
   }
-  total = buf[kSelThreads - 1];
-  int r = buf[t] - v;
+  return v;
+}
+
+// Inclusive prefix sum of one value per thread over the block (kSelThreads
+// threads, in thread order); also returns the total.  `wsum` holds one int
+// per wave.  Contains two barriers.
+__device__ int block_inclusive_scan(int v, int *wsum, int &total) {
+  const int w = threadIdx.x >> 6;
+  const int x = wave_inclusive_scan(v);
+  if ((threadIdx.x & 63) == 63) wsum[w] = x;
   __syncthreads();
-  return r;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int u = 0; u < kSelThreads / 64; u++) {
+    before += (u < w) ? wsum[u] : 0;
+    all += wsum[u];
+  }
+  total = all;
+  __syncthreads();  // wsum may be rewritten by the next call
+  return before + x;
 }
 
 // One workgroup per (b, h_q, query block i).
@@ -74,7 +86,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
   extern __shared__ uint64_t keys[];  // [n_valid]
   __shared__ double qrow[128];
   __shared__ int hist[256];
-  __shared__ int scan_buf[kSelThreads];
+  __shared__ int wsum[kSelThreads / 64];
   __shared__ int s_digit, s_above;
 
   const int nb = a.N / 64;
@@ -128,14 +140,15 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
         if ((kj & pmask) == prefix) atomicAdd(&hist[(kj >> shift) & 255], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        int above = 0, dgt = 255;
-        for (; dgt > 0; dgt--) {
-          if (above + hist[dgt] >= remaining) break;
-          above += hist[dgt];
-        }
-        s_digit = dgt;
-        s_above = above;
+      // the digit whose bin holds the remaining-th largest candidate: thread
+      // t takes digit 255 - t, so the inclusive scan counts the candidates
+      // at or above that digit; exactly one thread (a non-empty bin) crosses
+      const int cnt = hist[255 - tid];
+      int ncand;
+      const int at_or_above = block_inclusive_scan(cnt, wsum, ncand);
+      if (at_or_above >= remaining && at_or_above - cnt < remaining) {
+        s_digit = 255 - tid;
+        s_above = at_or_above - cnt;
       }
       __syncthreads();
       remaining -= s_above;
@@ -149,7 +162,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
     for (int j = j0; j < j1; j++)
       if (j != 0 && j != i && keys[j] == prefix) neq++;
     int tot;
-    int rank = block_exclusive_scan(neq, scan_buf, tot);
+    int rank = block_inclusive_scan(neq, wsum, tot) - neq;
     // mark the FP16 set in the key array: 1 = FP16, 0 = FP4
     for (int j = j0; j < j1; j++) {
       uint64_t kj = keys[j];
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
   int c16 = 0;
   for (int j = j0; j < j1; j++) c16 += (int)keys[j];
   int tot16;
-  int p16 = block_exclusive_scan(c16, scan_buf, tot16);
+  int p16 = block_inclusive_scan(c16, wsum, tot16) - c16;
   int p4 = tot16 + (j0 - p16);  // FP4 entries before this chunk = blocks before it minus FP16 ones
   for (int j = j0; j < j1; j++) {
     if (keys[j])
