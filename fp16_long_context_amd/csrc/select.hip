@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
   __shared__ double qrow[128];
   __shared__ int hist[256];
   __shared__ int wsum[kSelThreads / 64];
-  __shared__ int s_digit, s_above;
+  __shared__ int s_digit, s_above, s_count;
 
   const int nb = a.N / 64;
   const int64_t row = blockIdx.x;  // = (b*Hq + h)*nb + i
@@ -127,7 +127,10 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
     }
     __syncthreads();
     // radix select (8 bits per pass, most significant first) of the kextra-th
-    // largest key among the non-forced blocks
+    // largest key among the non-forced blocks.  After a pass, the candidates
+    // whose key starts with `prefix` (under pmask) hold the `remaining`
+    // largest not yet taken; if they are exactly that many, every one of
+    // them is taken and the search stops early.
     uint64_t prefix = 0, pmask = 0;
     int remaining = kextra;
     for (int pass = 0; pass < 8; pass++) {
@@ -149,18 +152,22 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
       if (at_or_above >= remaining && at_or_above - cnt < remaining) {
         s_digit = 255 - tid;
         s_above = at_or_above - cnt;
+        s_count = cnt;
       }
       __syncthreads();
       remaining -= s_above;
       prefix |= (uint64_t)s_digit << shift;
       pmask |= (uint64_t)255 << shift;
+      const bool done = s_count == remaining;
       __syncthreads();
+      if (done) break;
     }
-    // prefix is the threshold key T: take every key > T and the `remaining`
-    // lowest-index keys == T
+    // prefix (under pmask) is the threshold T: take every key whose masked
+    // value is > T and the `remaining` lowest-index keys whose masked value
+    // is == T (all of them when the search stopped early)
     int neq = 0;
     for (int j = j0; j < j1; j++)
-      if (j != 0 && j != i && keys[j] == prefix) neq++;
+      if (j != 0 && j != i && (keys[j] & pmask) == prefix) neq++;
     int tot;
     int rank = block_inclusive_scan(neq, wsum, tot) - neq;
     // mark the FP16 set in the key array: 1 = FP16, 0 = FP4
@@ -169,9 +176,9 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
       int sel;
       if (j == 0 || j == i)
         sel = 1;
-      else if (kj > prefix)
+      else if ((kj & pmask) > prefix)
         sel = 1;
-      else if (kj == prefix)
+      else if ((kj & pmask) == prefix)
         sel = (rank++ < remaining);
       else
         sel = 0;
