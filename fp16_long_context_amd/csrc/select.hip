@@ -81,7 +81,25 @@ __device__ int block_inclusive_scan(int v, int *wsum, int &total) {
   return before + x;
 }
 
+// Score of query block i against key block j: the fp64 fma chain over the
+// D channels in order.  The K means are loaded 16 channels at a time, so 16
+// loads are in flight before their fmas.
+template <int D>
+__device__ __forceinline__ double block_score(const double *qrow, const float *kT, const int nb, const int j) {
+  double s = 0.0;
+#pragma unroll 1
+  for (int c0 = 0; c0 < D; c0 += 16) {
+    float kv[16];
+#pragma unroll
+    for (int u = 0; u < 16; u++) kv[u] = kT[(int64_t)(c0 + u) * nb + j];
+#pragma unroll
+    for (int u = 0; u < 16; u++) s = fma(qrow[c0 + u], (double)kv[u], s);
+  }
+  return s;
+}
+
 // One workgroup per (b, h_q, query block i).
+template <int D>
 __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a) {
   extern __shared__ uint64_t keys[];  // [n_valid]
   __shared__ double qrow[128];
@@ -120,11 +138,7 @@ __global__ __launch_bounds__(kSelThreads) void score_select_kernel(SelectArgs a)
     __syncthreads();
     // scores: strided j for coalesced reads of the transposed K means
     const float *kT = a.kbarT + (int64_t)(b * a.Hkv + g) * a.d * nb;
-    for (int j = tid; j < nv; j += kSelThreads) {
-      double s = 0.0;
-      for (int c = 0; c < a.d; c++) s = fma(qrow[c], (double)kT[(int64_t)c * nb + j], s);
-      keys[j] = order_key(s);
-    }
+    for (int j = tid; j < nv; j += kSelThreads) keys[j] = order_key(block_score<D>(qrow, kT, nb, j));
     __syncthreads();
     // radix select (8 bits per pass, most significant first) of the kextra-th
     // largest key among the non-forced blocks.  After a pass, the candidates
@@ -216,10 +230,13 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(pool_kernel<false>, dim3(grid(BHq * nb * a.d)), dim3(256), 0, st, a.q16, a.qbar, BHq, a.N, a.d);
   hipLaunchKernelGGL(pool_kernel<true>, dim3(grid(BHk * nb * a.d)), dim3(256), 0, st, a.k16, a.kbarT, BHk, a.N, a.d);
   const size_t lds = sizeof(uint64_t) * (size_t)nb;
-  hipError_t e = hipFuncSetAttribute((const void *)score_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  const void *fn = a.d == 64 ? (const void *)score_select_kernel<64> : (const void *)score_select_kernel<128>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(score_select_kernel, dim3((unsigned)(BHq * nb)), dim3(kSelThreads), lds, st, a);
+  if (a.d == 64)
+    hipLaunchKernelGGL(score_select_kernel<64>, dim3((unsigned)(BHq * nb)), dim3(kSelThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL(score_select_kernel<128>, dim3((unsigned)(BHq * nb)), dim3(kSelThreads), lds, st, a);
   return hipGetLastError();
 }
 
