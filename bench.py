@@ -254,25 +254,9 @@ def main():
 def quality(binding, torch, qz, w, needles, frac, dev):
     """Planted-needle check: relative Frobenius error of frac and of frac=0
     against frac=1, over all rows and over the rows that look up a needle."""
-    outs = {}
-    for f in (1.0, frac, 0.0):
-        idx, n16 = binding.select(qz["q16"], qz["k16"], f, True)
-        outs[f], _ = binding.attn_fwd(qz, idx, n16, True)
-        del idx, n16
-    ref = outs[1.0]
-    rows = torch.tensor([(b * w.Hq + hq) * w.N + t for (b, kvh, hq, p, t) in needles], device=dev)
-    res = {}
-    for f, name in ((frac, "mixed"), (0.0, "fp4")):
-        d_all = torch.linalg.vector_norm((outs[f] - ref).reshape(-1)).item() / torch.linalg.vector_norm(ref).item()
-        r2 = ref.reshape(-1, w.d)[rows]
-        d_ndl = (torch.linalg.vector_norm(outs[f].reshape(-1, w.d)[rows] - r2) / torch.linalg.vector_norm(r2)).item()
-        res[f"err_{name}"] = d_all
-        res[f"needle_err_{name}"] = d_ndl
-    res["frac"] = frac
-    res["mixed_below_fp4"] = bool(res["err_mixed"] < res["err_fp4"] and res["needle_err_mixed"] < res["needle_err_fp4"])
-    res["gap_recovered"] = 1.0 - res["err_mixed"] / res["err_fp4"]
-    res["needle_gap_recovered"] = 1.0 - res["needle_err_mixed"] / res["needle_err_fp4"]
-    return {k: (round(v, 6) if isinstance(v, float) else v) for k, v in res.items()}
+    from fp16_long_context_amd.quality import errors
+
+    return errors(binding, torch, qz, w, needles, frac)
 
 
 if __name__ == "__main__":

@@ -160,3 +160,38 @@ def test_redo_walk_on_overflow():
     # head 0 (block 7): score ~ 12 |q|^2 ~ 1500, x ~ 190 log2 units
     k[0, 0, 200] = (12.0 * q[0, 0, 450].float()).to(q.dtype)
     run_case(q, k, v, 0.0, label="redo walk")
+
+
+@pytest.mark.parametrize("delta", [0, 5, 15])
+def test_single_fp16_block_lists(delta):
+    """Lists that are not the selection's (one FP16 block per row block, at
+    a fixed diagonal offset, nothing forced), as the error-attribution study
+    feeds them: the attention must still match the oracle on the same lists."""
+    from fp16_long_context_amd.quality import offset_lists
+
+    x = synth.generate("llama8b_16k", N=1024)
+    q, k, v = x["q"], x["k"], x["v"]
+    B, Hq, N, d = q.shape
+    nb = N // 64
+    say(f"[case] single FP16 block at offset {delta}, llama8b@1k")
+    # the oracle's lists, written out row by row
+    idx_o, n16_o = [], np.zeros((B, Hq, nb), dtype=np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(nb):
+                j16 = i - delta
+                idx_o += ([j16] if j16 >= 0 else []) + [j for j in range(i + 1) if j != j16]
+                n16_o[b, h, i] = 1 if j16 >= 0 else 0
+    idx_o = np.asarray(idx_o, dtype=np.int32)
+    dev = torch.device("cuda:0")
+    qz = binding.quantize(q.to(dev), k.to(dev), v.to(dev))
+    idx, n16 = offset_lists(B, Hq, nb, delta, dev)
+    assert np.array_equal(idx.cpu().numpy(), idx_o) and np.array_equal(n16.cpu().numpy(), n16_o)
+    out, _ = binding.attn_fwd(qz, idx, n16, True)
+    qz_o = oracle.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "bf16")
+    rows = oracle.all_rows(B, Hq, N)
+    res = oracle.attn_rows(qz_o, {"idx": idx_o, "n16": n16_o}, rows, True)
+    og = out.reshape(-1, d).cpu().numpy().astype(np.float64)[rows]
+    err = np.abs(og - res["out"]).max() / np.abs(res["out"]).max()
+    say(f"[case] offset {delta}: max|dO|/max|O| = {err:.3e}")
+    assert err <= TOL
