@@ -17,7 +17,10 @@ Parity status per function:
                                 list invariants, a worked example)
   attn_rows                     pinned (frac=1 against textbook softmax
                                 attention, FP4-exact inputs against textbook
-                                attention, closed forms, split-merge)
+                                attention, closed forms, split-merge);
+                                rowsum="weights": V = 1 gives O = 1 exactly,
+                                frac=1 against textbook attention, split-merge,
+                                closed forms
 """
 from __future__ import annotations
 
@@ -45,7 +48,7 @@ def build() -> str:
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_SO):
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
             build()
         L = ctypes.CDLL(_SO)
         P = ctypes.c_void_p
@@ -64,7 +67,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_list_entries.restype = i64
         L.oracle_select.argtypes = [i32] * 6 + [f64] + [P] * 7
         L.oracle_select.restype = i32
-        L.oracle_attn_rows.argtypes = [i32] * 6 + [f32] + [P] * 9 + [P, P, P, i64, P, P, P, P, P, P]
+        L.oracle_attn_rows.argtypes = [i32] * 6 + [f32] + [P] * 9 + [P, P, P, i64, P, P, P, P, P, P, i32]
         L.oracle_attn_rows.restype = i32
         _lib = L
     return _lib
@@ -164,9 +167,15 @@ def row_lists(sel: dict, B, Hq, N, causal, b, h, i):
     return row[:c], row[c:]
 
 
-def attn_rows(qz: dict, sel: dict, rows, causal: bool = True, sm_scale: float = 0.0, blk_keep=None) -> dict:
+ROWSUM = {"p": 0, "weights": 1}
+
+
+def attn_rows(qz: dict, sel: dict, rows, causal: bool = True, sm_scale: float = 0.0, blk_keep=None,
+              rowsum: str = "p") -> dict:
     """Mixed-precision attention for the flat output rows ((b*Hq + h)*N + t).
 
+    rowsum "p": the row sum adds the unquantized p; "weights": it adds the
+    weights the P.V products use (fp16(p), dequantized MXFP4 P).
     Returns out [R,d] (normalised), lse [R], acc [R,d] (unnormalised), l [R], m [R]."""
     q16 = qz["q16"]
     B, Hq, N, d = q16.shape
@@ -180,7 +189,8 @@ def attn_rows(qz: dict, sel: dict, rows, causal: bool = True, sm_scale: float = 
             for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")]
     rc = lib().oracle_attn_rows(B, Hq, Hkv, N, d, int(causal), float(sm_scale), *[_p(a) for a in arrs],
                                 _p(_c(sel["idx"], np.int32)), _p(_c(sel["n16"], np.int32)), _p(rows), R, _p(keep),
-                                _p(res["out"]), _p(res["lse"]), _p(res["acc"]), _p(res["l"]), _p(res["m"]))
+                                _p(res["out"]), _p(res["lse"]), _p(res["acc"]), _p(res["l"]), _p(res["m"]),
+                                ROWSUM[rowsum])
     if rc != 0:
         raise ValueError("oracle_attn_rows: bad arguments or malformed lists")
     return res

@@ -343,6 +343,15 @@ int oracle_select(int B, int Hq, int Hkv, int N, int d, int causal, double frac,
  * scores).  A row with no participating key gets M = -inf, l = 0, acc = 0,
  * out = 0, lse = -inf.
  *
+ * rowsum selects what the row sum l adds up:
+ *   0  the unquantized p of every key (the row sum of the online softmax
+ *      before any rounding of P; the reading the main path follows);
+ *   1  the weights the P.V products actually use: fp16(p) on FP16 tiles and
+ *      the dequantized MXFP4 code of p on FP4 tiles, so the output is a
+ *      convex combination of V rows with exactly those weights (the
+ *      alternative reading: normalisation by the quantized weights).
+ * acc and (for rowsum 1) l take the same terms in the same order.
+ *
  * v16 here is [B,Hkv,N,d] (token-major).
  */
 int oracle_attn_rows(int B, int Hq, int Hkv, int N, int d, int causal, float sm_scale, const uint16_t *q16,
@@ -350,8 +359,8 @@ int oracle_attn_rows(int B, int Hq, int Hkv, int N, int d, int causal, float sm_
                      const uint8_t *k4, const uint8_t *k4s, const uint8_t *v4, const uint8_t *v4s,
                      const int32_t *idx, const int32_t *n16, const int64_t *rows, int64_t nrows,
                      const uint8_t *blk_keep, double *out, double *lse, double *acc_out, double *l_out,
-                     double *m_out) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N % 64 || d % 32) return ORC_EINVAL;
+                     double *m_out, int rowsum) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N % 64 || d % 32 || rowsum < 0 || rowsum > 1) return ORC_EINVAL;
   int nb = N / 64;
   int64_t per = causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
   /* score scale in log2 units: c = fl32(sm_scale * log2(e)), sm_scale <= 0 -> fl32(1/sqrt(d)) */
@@ -421,7 +430,7 @@ int oracle_attn_rows(int B, int Hq, int Hkv, int N, int d, int causal, float sm_
       for (int64_t key = 0; key < nkeys; key++)
         if (live[key]) {
           p[key] = (double)(float)exp2(x[key] - M);
-          l += p[key];
+          if (rowsum == 0) l += p[key];
         }
       for (int j = 0; j < nb; j++) {
         if (prec[j] == 16) {
@@ -429,6 +438,7 @@ int oracle_attn_rows(int B, int Hq, int Hkv, int N, int d, int causal, float sm_
             int64_t key = (int64_t)j * 64 + kk;
             if (!live[key]) continue;
             double p16 = half_bits_to_double(double_to_half_bits(p[key]));
+            if (rowsum == 1) l += p16;
             for (int ch = 0; ch < d; ch++) acc[ch] += p16 * half_bits_to_double(v16[(kvh * N + key) * d + ch]);
           }
         } else if (prec[j] == 4) {
@@ -437,6 +447,11 @@ int oracle_attn_rows(int B, int Hq, int Hkv, int N, int d, int causal, float sm_
             uint8_t pc[32];
             /* masked keys enter the group as zeros */
             uint8_t ps = mx_encode_group(p + k0, 32, pc);
+            if (rowsum == 1) {
+              double gw = 0.0; /* exact group sum of the codes' values */
+              for (int e = 0; e < 32; e++) gw += e2m1_value(pc[e]);
+              l += e8m0_value(ps) * gw;
+            }
             for (int ch = 0; ch < d; ch++) {
               const uint8_t *vrow = v4 + (kvh * d + ch) * (N / 2);
               double gs = 0.0; /* exact group sum */

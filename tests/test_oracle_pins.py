@@ -411,3 +411,69 @@ def test_frac0_within_p_quantization_bound_of_dequantized_attention(orc):
     # slack: the oracle rounds p to fp32 before summing and quantizing
     assert np.all(diff <= bound + 1e-6 * np.abs(ref).max())
     assert diff.max() > 1e-4  # and P quantization really is in effect
+
+
+# ------------------------------------------- row sum over the quantized weights
+# The alternative reading of the row sum: l adds the weights the P.V products
+# use (fp16(p) on FP16 tiles, the dequantized MXFP4 P on FP4 tiles).
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.05, 0.3, 1.0])
+def test_weights_rowsum_constant_values_give_exactly_one(orc, frac):
+    # V = 1 everywhere: fp16 V is 1.0 and every MXFP4 V group dequantizes to
+    # exactly 1.0, so acc and l add the same terms in the same order and
+    # O = acc / l = 1 exactly; under the unquantized row sum it is not
+    q, k, _ = synth.random_qkv(1, 2, 1, 512, 64, "bf16", seed=41, scale=1.5)
+    v = torch.ones((1, 1, 512, 64), dtype=torch.bfloat16)
+    qz = orc.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "bf16")
+    sel = orc.select(qz["q16"], qz["k16"], frac, True)
+    rows = orc.all_rows(1, 2, 512)
+    w = orc.attn_rows(qz, sel, rows, rowsum="weights")
+    assert np.array_equal(w["out"], np.ones_like(w["out"]))
+    p = orc.attn_rows(qz, sel, rows, rowsum="p")
+    assert np.array_equal(p["acc"], w["acc"]) and np.array_equal(p["m"], w["m"])
+    if frac < 1.0:
+        assert np.abs(p["out"] - 1.0).max() > 1e-3  # FP4 P moves the plain row sum off
+    assert np.abs(p["out"] - 1.0).max() < 0.5
+
+
+@pytest.mark.parametrize("causal,d", [(True, 64), (False, 128)])
+def test_weights_rowsum_frac1_equals_textbook_fp16_attention(orc, causal, d):
+    q, k, v = synth.random_qkv(1, 2, 2, 256, d, "bf16", seed=43, scale=1.5)
+    qz = orc.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "bf16")
+    sel = orc.select(qz["q16"], qz["k16"], 1.0, causal)
+    res = orc.attn_rows(qz, sel, orc.all_rows(1, 2, 256), causal, rowsum="weights")
+    want = softmax_attention(half_vals(qz["q16"]), half_vals(qz["k16"]), half_vals(qz["v16"]), causal)
+    err = np.abs(res["out"].reshape(want.shape) - want).max() / np.abs(want).max()
+    assert err < 5e-4
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.3])
+def test_weights_rowsum_fp4_exact_inputs_equal_textbook_attention(orc, frac):
+    # every P is exact in MXFP4 and fp16 here, so both row sums coincide
+    q, k, v = fp4_exact_inputs(19)
+    ln2 = float(np.float32(np.log(2.0)))
+    qz = orc.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "fp16")
+    sel = orc.select(qz["q16"], qz["k16"], frac, True)
+    res = orc.attn_rows(qz, sel, orc.all_rows(1, 2, 256), True, ln2, rowsum="weights")
+    want = softmax_attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), True, sm_scale=1 / np.log2(np.e))
+    np.testing.assert_allclose(res["out"].reshape(want.shape), want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("frac,tol", [(0.0, 1e-12), (0.2, 1e-6)])
+def test_weights_rowsum_split_merge_equals_one_pass(orc, frac, tol):
+    q, k, v = synth.random_qkv(1, 2, 1, 1024, 64, "bf16", seed=47, scale=2.0)
+    qz = orc.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "bf16")
+    sel = orc.select(qz["q16"], qz["k16"], frac, True)
+    rows = np.arange(2 * 1024)
+    one = orc.attn_rows(qz, sel, rows, rowsum="weights")
+    g = np.random.default_rng(1)
+    for parts in (2, 4):
+        lab = g.integers(0, parts, size=16)
+        st = [orc.attn_rows(qz, sel, rows, blk_keep=(lab == p_), rowsum="weights") for p_ in g.permutation(parts)]
+        M = np.full(rows.size, -np.inf)
+        for s_ in st:
+            M = np.maximum(M, s_["m"])
+        acc = sum(np.where(np.isfinite(s_["m"])[:, None], s_["acc"] * np.exp2(s_["m"] - M)[:, None], 0) for s_ in st)
+        l = sum(np.where(np.isfinite(s_["m"]), s_["l"] * np.exp2(s_["m"] - M), 0) for s_ in st)
+        assert np.abs(acc / l[:, None] - one["out"]).max() <= tol * np.abs(one["out"]).max()
