@@ -22,7 +22,11 @@ Prints one JSON line:
              same workload, on this host's cores;
   kernels    quantize / select / attention times and algorithmic GB/s;
   quality    planted-needle check: error of frac=0.05 and of frac=0 against
-             frac=1 (all-FP16) output.
+             frac=1 (all-FP16) output;
+  alt_rowsum_weights  the attention call under the other row-sum reading
+             (thrift_attn_fwd_wsum: normalised by the quantized weights, the
+             FP4 row sums from one more MFMA), timed alone over the same
+             steps, with its own quality figures.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--frac F]
 """
@@ -136,6 +140,8 @@ def main():
     ap.add_argument("--frac", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quality", action="store_true")
+    ap.add_argument("--no-alt", action="store_true",
+                    help="skip the timing and quality of the attention normalised by the quantized weights")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -242,9 +248,30 @@ def main():
             "attn_ms": round(t_a, 4), "attn_TFLOPs": round(achieved, 2), "hbm_peak_GBps": PEAK_HBM,
         },
     }
+    if not args.no_alt:
+        # the same attention call normalised by the quantized weights
+        # (thrift_attn_fwd_wsum), timed alone on the same lists and inputs
+        for _ in range(2):
+            binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws, rowsum="weights")
+        torch.cuda.synchronize()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
+        for _ in range(args.steps):
+            binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws, rowsum="weights")
+        eb.record()
+        torch.cuda.synchronize()
+        t_w = ea.elapsed_time(eb) / args.steps
+        result["alt_rowsum_weights"] = {
+            "entry": "thrift_attn_fwd_wsum", "attn_ms": round(t_w, 4),
+            "attn_TFLOPs": round(F / (t_w * 1e-3) / 1e12, 2), "roofline_frac": round(F / (t_w * 1e-3) / 1e12 / peak, 4)}
+        log(f"attention normalised by the quantized weights: {t_w:.3f} ms")
     if not args.no_quality:
         result["quality"] = quality(binding, torch, qz, w, x["needles"], frac, dev)
         log(f"quality {result['quality']}")
+        if not args.no_alt:
+            from fp16_long_context_amd.quality import errors
+
+            result["alt_rowsum_weights"]["quality"] = errors(binding, torch, qz, w, x["needles"], frac, "weights")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, w, frac)
         log(f"cpu baseline {result['cpu_baseline']['value']:.3e} TFLOP/s on {result['cpu_baseline']['cores']} threads")

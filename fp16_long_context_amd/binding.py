@@ -29,7 +29,7 @@ class Shape(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("thrift_quantize", "thrift_select_workspace_bytes", "thrift_list_entries", "thrift_select",
-           "thrift_attn_fwd", "thrift_attn_workspace_bytes", "thrift_status_str")
+           "thrift_attn_fwd", "thrift_attn_fwd_wsum", "thrift_attn_workspace_bytes", "thrift_status_str")
 
 
 def lib() -> ctypes.CDLL:
@@ -50,8 +50,9 @@ def lib() -> ctypes.CDLL:
         L.thrift_list_entries.restype = i64
         L.thrift_select.argtypes = [SP, f64, P, P, P, P, P, sz, P]
         L.thrift_select.restype = i32
-        L.thrift_attn_fwd.argtypes = [SP, f32] + [P] * 11 + [P, i32, P, P, sz, P]
-        L.thrift_attn_fwd.restype = i32
+        for fn in (L.thrift_attn_fwd, L.thrift_attn_fwd_wsum):
+            fn.argtypes = [SP, f32] + [P] * 11 + [P, i32, P, P, sz, P]
+            fn.restype = i32
         L.thrift_attn_workspace_bytes.argtypes = [SP]
         L.thrift_attn_workspace_bytes.restype = sz
         L.thrift_status_str.argtypes = [i32]
@@ -159,9 +160,14 @@ def attn_workspace_bytes(B, Hq, Hkv, N, d, causal=True) -> int:
 
 
 def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True, sm_scale: float = 0.0,
-             out_dtype=torch.float32, want_lse: bool = False, out=None, lse=None, workspace=None):
+             out_dtype=torch.float32, want_lse: bool = False, out=None, lse=None, workspace=None,
+             rowsum: str = "p"):
     """Fused FP16/MXFP4 attention.  Returns (out [B,Hq,N,d], lse [B,Hq,N] or None).
-    out, lse and the workspace (uint8, thrift_attn_workspace_bytes) may be preallocated."""
+    out, lse and the workspace (uint8, thrift_attn_workspace_bytes) may be preallocated.
+    rowsum "p" (thrift_attn_fwd): the row sum adds the unquantized p;
+    "weights" (thrift_attn_fwd_wsum): it adds the weights the P.V products use."""
+    if rowsum not in ("p", "weights"):
+        raise ThriftError("rowsum must be 'p' or 'weights'")
     q16 = qz["q16"]
     B, Hq, N, d = q16.shape
     Hkv = qz["k16"].shape[1]
@@ -179,7 +185,8 @@ def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True
         raise ThriftError("unsupported shape")
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q16.device)
-    rc = L.thrift_attn_fwd(ctypes.byref(s), float(sm_scale),
+    fn = L.thrift_attn_fwd if rowsum == "p" else L.thrift_attn_fwd_wsum
+    rc = fn(ctypes.byref(s), float(sm_scale),
                            *[_ptr(qz[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
                            _ptr(idx), _ptr(n16), _ptr(out), _DT[out.dtype], _ptr(lse), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(q16.device))

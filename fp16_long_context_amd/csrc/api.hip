@@ -97,10 +97,10 @@ size_t thrift_attn_workspace_bytes(const thrift_shape *s) {
   return attn_workspace_bytes(s->B, s->Hq, s->N, s->d);
 }
 
-int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
-                    const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
-                    const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype, float *lse,
-                    void *workspace, size_t ws_bytes, void *stream) {
+static int attn_fwd_common(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
+                           const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
+                           const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
+                           float *lse, void *workspace, size_t ws_bytes, void *stream, int rowsum) {
   int rc = check_shape(s);
   if (rc != THRIFT_OK) return rc;
   if (out_dtype != THRIFT_F16 && out_dtype != THRIFT_BF16 && out_dtype != THRIFT_F32) return THRIFT_EINVAL;
@@ -118,10 +118,27 @@ int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, cons
   a.idx = idx; a.n16 = n16; a.out = out; a.lse = lse; a.ws = (float *)workspace;
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
   a.out_dtype = out_dtype;
+  a.rowsum = rowsum;
   // score scale in log2 units, rounded once to fp32
   const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)s->d));
   a.c = (float)((double)sm * 1.4426950408889634074);
   return launch_attn_fwd(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
+int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
+                    const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
+                    const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype, float *lse,
+                    void *workspace, size_t ws_bytes, void *stream) {
+  return attn_fwd_common(s, sm_scale, q16, k16, v16, q4, q4s, k4, k4s, v4, v4s, idx, n16, out, out_dtype, lse,
+                         workspace, ws_bytes, stream, 0);
+}
+
+int thrift_attn_fwd_wsum(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
+                         const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
+                         const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
+                         float *lse, void *workspace, size_t ws_bytes, void *stream) {
+  return attn_fwd_common(s, sm_scale, q16, k16, v16, q4, q4s, k4, k4s, v4, v4s, idx, n16, out, out_dtype, lse,
+                         workspace, ws_bytes, stream, 1);
 }
 
 }  // extern "C"

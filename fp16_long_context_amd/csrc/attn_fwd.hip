@@ -175,7 +175,9 @@ __device__ __forceinline__ float lane_max32(const float16v (&s)[2]) {
 // acc and the row sum by an exact power of two), replaces s by
 // p = 2^(s*c - M) and adds the lane's p to l_part.  Returns the lane's
 // largest raw score (-inf if all masked).
-template <int CB, bool MASK>
+// LS picks what the row sum adds: 0 the fp32 p, 1 fp16(p) (p is also left
+// rounded to fp16 in s), 2 nothing (the caller adds the dequantized FP4 P).
+template <int CB, bool MASK, int LS = 0>
 __device__ __forceinline__ float softmax_step(float16v (&s)[2], float16v (&acc)[CB], float &M, float &l_part,
                                               const float c, const int lh, const int qpos) {
   if (MASK) {
@@ -204,11 +206,31 @@ __device__ __forceinline__ float softmax_step(float16v (&s)[2], float16v (&acc)[
   for (int r = 0; r < 16; r++) {
     s[0][r] = __builtin_amdgcn_exp2f(fmaf(s[0][r], c, negM));
     s[1][r] = __builtin_amdgcn_exp2f(fmaf(s[1][r], c, negM));
+    if (LS == 1) {
+      s[0][r] = (float)(_Float16)s[0][r];
+      s[1][r] = (float)(_Float16)s[1][r];
+    }
     l0 += s[0][r];
     l1 += s[1][r];
   }
-  l_part += l0 + l1;
+  if (LS != 2) l_part += l0 + l1;
   return lane_max;
+}
+
+// Sum of the 32 E2M1 values packed in pw (this lane's P codes), times the
+// group scale 2^(psb - 127): the lane's dequantized P.  The code sums are
+// exact in fp32 (at most 32 * 6, multiples of 1/2).
+__device__ __forceinline__ float fp4_code_sum(const uint32_t (&pw)[4], const int psb) {
+  float t = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pw[w], 1.0f, 0);
+    const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pw[w], 1.0f, 1);
+    const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pw[w], 1.0f, 2);
+    const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pw[w], 1.0f, 3);
+    t += ((f0[0] + f0[1]) + (f1[0] + f1[1])) + ((f2[0] + f2[1]) + (f3[0] + f3[1]));
+  }
+  return ldexpf(t, psb - 127);
 }
 
 // K operands (MXFP4 codes and scale bytes) of an FP4 tile's QK product.
@@ -349,9 +371,13 @@ __device__ __forceinline__ void fp4_scores(const uint8_t *kst, const uint8_t *vs
 // FP4 tile, second half: p (this lane's 32 values, one aligned 32-key group,
 // relative to the max the exponent used) re-quantized to MXFP4, and
 // O^T += V^T P^T.
-template <int CB>
+// WS 1: also adds the lane's dequantized P to *l_add (VALU); WS 2: also
+// accumulates the dequantized P of every key into lacc with one more scaled
+// MFMA against E2M1 ones (every row of lacc then holds the row's sum).
+template <int CB, int WS = 0>
 __device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
-                                       const int4v (&va)[CB], const int (&vs)[CB], float16v (&acc)[CB]) {
+                                       const int4v (&va)[CB], const int (&vs)[CB], float16v (&acc)[CB],
+                                       float *l_add = nullptr, float16v *lacc = nullptr) {
   const int psb = mx_scale_byte(amax);
   const float div = mx_scale_divisor(psb);
   uint32_t pw[4];
@@ -372,10 +398,16 @@ __device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
     int8v a8 = {va[cb][0], va[cb][1], va[cb][2], va[cb][3], 0, 0, 0, 0};
     acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, pb, acc[cb], 4, 4, 0, vs[cb], 0, psb);
   }
+  if (WS == 1) *l_add += fp4_code_sum(pw, psb);
+  if (WS == 2) {
+    // E2M1 code 2 (1.0) in every nibble, scale byte 127 (2^0)
+    const int8v ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+    *lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, *lacc, 4, 4, 0, 127, 0, psb);
+  }
 }
 
 // One FP4 tile (general walk): the running max may rise, rescaling acc.
-template <int D, int HPW, bool MASK>
+template <int D, int HPW, bool MASK, bool W = false>
 __device__ __forceinline__ void tile_fp4(const uint8_t *kst, const uint8_t *vst, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
                                          float16v (&acc)[D / 32], float &M, float &l_part, const float c,
                                          const int col, const int lh, const int qpos) {
@@ -384,8 +416,8 @@ __device__ __forceinline__ void tile_fp4(const uint8_t *kst, const uint8_t *vst,
   int4v va[CB];
   int vs[CB];
   fp4_scores<D, HPW, MASK>(kst, vst, qf4, qs4, col, lh, qpos, s, va, vs);
-  const float lane_max = softmax_step<CB, false>(s, acc, M, l_part, c, lh, qpos);
-  fp4_pv<CB>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, -M)), va, vs, acc);
+  const float lane_max = softmax_step<CB, false, W ? 2 : 0>(s, acc, M, l_part, c, lh, qpos);
+  fp4_pv<CB, W ? 1 : 0>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, -M)), va, vs, acc, &l_part);
 }
 
 // Softmax and P.V of one FP4 tile whose scores s are already computed,
@@ -395,26 +427,28 @@ __device__ __forceinline__ void tile_fp4(const uint8_t *kst, const uint8_t *vst,
 // group scale comes from the largest p of the lane's 32-key group (the MXFP4
 // rule's amax, taken after the exponentials).  A group with amax above kMaxP
 // (or not finite) sets `overflow`.
-template <int CB>
+template <int CB, bool W = false>
 __device__ __forceinline__ void fp4_fixed_rest(float16v (&s)[2], const int4v (&va)[CB], const int (&vs)[CB],
                                                float16v (&acc)[CB], const float M, float &l_part, bool &overflow,
-                                               const float c) {
+                                               const float c, float16v *lacc = nullptr) {
   const float negM = -M;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     s[0][r] = __builtin_amdgcn_exp2f(fmaf(s[0][r], c, negM));
     s[1][r] = __builtin_amdgcn_exp2f(fmaf(s[1][r], c, negM));
   }
-  float l0 = s[0][0], l1 = s[1][0];
+  if (!W) {
+    float l0 = s[0][0], l1 = s[1][0];
 #pragma unroll
-  for (int r = 1; r < 16; r++) {
-    l0 += s[0][r];
-    l1 += s[1][r];
+    for (int r = 1; r < 16; r++) {
+      l0 += s[0][r];
+      l1 += s[1][r];
+    }
+    l_part += l0 + l1;
   }
-  l_part += l0 + l1;
   const float amax = lane_max32(s);
   overflow = overflow || !(amax <= kMaxP);
-  fp4_pv<CB>(s, amax, va, vs, acc);
+  fp4_pv<CB, W ? 2 : 0>(s, amax, va, vs, acc, nullptr, lacc);
 }
 
 // True if x is an infinity or a NaN (exponent field all ones); integer test,
@@ -424,7 +458,7 @@ __device__ __forceinline__ bool not_finite(float x) { return (__float_as_uint(x)
 // One FP16 tile for one wave: S^T from FP16 K and Q, P rounded to fp16,
 // O^T += V^T P^T with FP16 V.  st16 is the tile's FP16 region (K rows, then
 // channel-major V); qrow16 points at this lane's Q16 row in LDS.
-template <int D, int HPW, bool MASK>
+template <int D, int HPW, bool MASK, bool W = false>
 __device__ __forceinline__ void tile_fp16(const uint8_t *st16, const uint8_t *qrow16, float16v (&acc)[D / 32],
                                           float &M, float &l_part, const float c, const int col_in, const int lh,
                                           const int qpos) {
@@ -462,7 +496,7 @@ __device__ __forceinline__ void tile_fp16(const uint8_t *st16, const uint8_t *qr
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[u], qb[u], s[1], 0, 0, 0);
     }
   }
-  softmax_step<CB, MASK>(s, acc, M, l_part, c, lh, qpos);
+  softmax_step<CB, MASK, W ? 1 : 0>(s, acc, M, l_part, c, lh, qpos);
   // P in fp16; MFMA u consumes keys 32*lh + 8u + 0..7 of this lane
   half8 pb[4];
 #pragma unroll
@@ -669,7 +703,7 @@ struct Tile16 {
 // Online-softmax step on one 32-query x 32-key score tile s (this lane:
 // query col, keys 16(r/8) + 8 lh + r%8 of the half): as softmax_step, for a
 // tile in which every row has at least one valid key.
-template <int CB, bool MASK>
+template <int CB, bool MASK, bool W>
 __device__ __forceinline__ void softmax_half(float16v &s, float16v (&acc)[CB], float &M, float &l_part, const float c,
                                              const int key0, const int lh, const int qpos) {
   if (MASK) {
@@ -702,6 +736,10 @@ __device__ __forceinline__ void softmax_half(float16v &s, float16v (&acc)[CB], f
   for (int r = 0; r < 8; r++) {
     s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, negM));
     s[8 + r] = __builtin_amdgcn_exp2f(fmaf(s[8 + r], c, negM));
+    if (W) {  // the row sum adds the fp16 weights P.V uses
+      s[r] = (float)(_Float16)s[r];
+      s[8 + r] = (float)(_Float16)s[8 + r];
+    }
     l0 += s[r];
     l1 += s[8 + r];
   }
@@ -711,7 +749,7 @@ __device__ __forceinline__ void softmax_half(float16v &s, float16v (&acc)[CB], f
 // One 32-key half (keys 32 kh + 0..31) of an FP16 tile for one wave: S^T from
 // FP16 K and Q (K rows fed so that register r holds key 16(r/8) + 8 lh + r%8),
 // P rounded to fp16, O^T += V^T P^T with FP16 V.
-template <int D, bool MASK>
+template <int D, bool MASK, bool W>
 __device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const uint8_t *qrow16, const int kh,
                                                float16v (&acc)[D / 32], float &M, float &l_part, const float c,
                                                const int col, const int lh, const int qpos) {
@@ -742,7 +780,7 @@ __device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const uint8_
   }
 #pragma unroll
   for (int r = 0; r < 16; r++) s0[r] += s1[r];
-  softmax_half<CB, MASK>(s0, acc, M, l_part, c, 32 * kh, lh, qpos);
+  softmax_half<CB, MASK, W>(s0, acc, M, l_part, c, 32 * kh, lh, qpos);
   // P in fp16: MFMA u consumes keys 16u + 8 lh + 0..7 (registers 8u + 0..7)
   half8 pb[2];
 #pragma unroll
@@ -762,7 +800,7 @@ __device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const uint8_
   }
 }
 
-template <int D>
+template <int D, bool W>
 __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   using T = Tile<D, 1>;
   constexpr int CB = D / 32;
@@ -848,15 +886,15 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   // diagonal block is the last valid one): one unmasked body, no branches.
   for (int e = 0; e + 1 < cnt; e++)
     ring_step(e, [&](const uint8_t *st16, int) {
-      tile_fp16_half<D, false>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+      tile_fp16_half<D, false, W>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
     });
   if (cnt > 0)
     ring_step(cnt - 1, [&](const uint8_t *st16, int jc) {
       if (a.causal && jc == i) {
         // the upper key half of the diagonal has no valid key for the lower rows
-        if (!(kh == 1 && qhalf == 0)) tile_fp16_half<D, true>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+        if (!(kh == 1 && qhalf == 0)) tile_fp16_half<D, true, W>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
       } else {
-        tile_fp16_half<D, false>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+        tile_fp16_half<D, false, W>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
       }
     });
   // Merge the two key halves of each row (lane by lane: the same lane of the
@@ -925,7 +963,7 @@ __device__ __forceinline__ int *redo_flags(const AttnArgs &a) {
 // (block j in slots j % 2), with tile bodies that raise M whenever a block
 // needs it; then the rows are stored.  Same grid as the FP4 kernel; a
 // workgroup whose item was not flagged returns at once.
-template <int D, int HPW>
+template <int D, int HPW, bool W>
 __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
   using T = Tile<D, HPW>;
   constexpr int KS4 = D / 64, CB = D / 32;
@@ -990,14 +1028,14 @@ __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
       const uint8_t *s16 = slot16 + sl * T::FP16_BYTES, *ks4 = kslot + sl * T::KSLOT, *vs4 = vslot + sl * T::VSLOT;
       if (a.causal && j == nv - 1) {
         if (fc)
-          tile_fp16<D, HPW, true>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
+          tile_fp16<D, HPW, true, W>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
         else
-          tile_fp4<D, HPW, true>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+          tile_fp4<D, HPW, true, W>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
       } else {
         if (fc)
-          tile_fp16<D, HPW, false>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
+          tile_fp16<D, HPW, false, W>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
         else
-          tile_fp4<D, HPW, false>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+          tile_fp4<D, HPW, false, W>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
       }
     }
     wait_vmem();
@@ -1015,7 +1053,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
 // list, with the FP4 QK product one block ahead.  The walk is the same for
 // all waves (K/V tiles are shared in LDS); a head skips a block of its own
 // FP16 list by adding neither p to l nor P.V to the accumulator.
-template <int D, int HPW>
+template <int D, int HPW, bool W>
 __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   using T = Tile<D, HPW>;
   constexpr int NT = 128 * HPW;                  // threads
@@ -1071,6 +1109,11 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     l_part = pw[(D / 2 + 1) * 64 + lane];
   }
   bool overflow = false;
+  // row sums of the dequantized FP4 P of the fixed walk (weights row sum):
+  // every row of this MFMA tile holds the lane's column sum
+  float16v lacc;
+#pragma unroll
+  for (int r = 0; r < 16; r++) lacc[r] = 0.0f;
   __syncthreads();
 
   const Loader<D, 2 * HPW> ld(a, b, g, wave_u, lane);
@@ -1143,7 +1186,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     int4v va[CB];
     int vs[CB];
     fp4_vops_at<D, HPW>(k * T::VSLOT, fo, va, vs);
-    fp4_fixed_rest<CB>(s, va, vs, acc, M, l_part, overflow, c);
+    fp4_fixed_rest<CB, W>(s, va, vs, acc, M, l_part, overflow, c, &lacc);
   };
   // Step at walk position m (slot m % 2): loads the K and V of position m+1
   // into the other slot, then finishes position m if this wave's head has
@@ -1165,6 +1208,8 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     if (j0 >= nv) break;
     step(1);
   }
+  // both lane halves hold the full column sum: one half adds it
+  if (W && lh == 0) l_part += lacc[0];
   // the diagonal block (causal) for heads that have it on their FP4 list
   if (a.causal) {
     const uint32_t hd = fp16_heads<HPW>(mask, jend, head_bits);
@@ -1174,7 +1219,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
       wait_vmem();
       __syncthreads();
       if (head_ok && !((hd >> hl) & 1u))
-        tile_fp4<D, HPW, true>(kslot, vslot, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+        tile_fp4<D, HPW, true, W>(kslot, vslot, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
     }
   }
   // An FP4 group above kMaxP, or an accumulator or row sum that left the
@@ -1190,45 +1235,41 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   if (!flagged && head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
 }
 
-template <int D, int HPW>
+template <int D, int HPW, bool W>
 static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
   using T = Tile<D, HPW>;
   const int group = a.Hq / a.Hkv;
   const int chunks = (group + HPW - 1) / HPW;
   const unsigned nb = (unsigned)(a.N / 64);
-  hipError_t e = hipFuncSetAttribute((const void *)attn_f16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  hipError_t e = hipFuncSetAttribute((const void *)attn_f16_kernel<D, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      Tile16<D>::LDS);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           T::F4_LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_f16_kernel<D>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(256), Tile16<D>::LDS, st, a);
+  hipLaunchKernelGGL((attn_f16_kernel<D, W>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(256), Tile16<D>::LDS, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid4(nb * (unsigned)(a.B * a.Hkv * chunks));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW>), grid4, dim3(128 * HPW), T::F4_LDS, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, W>), grid4, dim3(128 * HPW), T::F4_LDS, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW>, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  e = hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          T::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_redo_kernel<D, HPW>), grid4, dim3(128 * HPW), T::LDS, st, a);
+  hipLaunchKernelGGL((attn_redo_kernel<D, HPW, W>), grid4, dim3(128 * HPW), T::LDS, st, a);
   return hipGetLastError();
 }
 
+template <int D, bool W>
+static hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
+  // two heads of a GQA group per FP4 workgroup when the group has two
+  return (a.Hq / a.Hkv >= 2) ? launch_one<D, 2, W>(a, st) : launch_one<D, 1, W>(a, st);
+}
+
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st) {
-  const int group = a.Hq / a.Hkv;
-#ifndef THRIFT_F4_HPW_MAX
-#define THRIFT_F4_HPW_MAX 2
-#endif
-  const int hpw = (group >= 4 && THRIFT_F4_HPW_MAX >= 4) ? 4 : ((group >= 2 && THRIFT_F4_HPW_MAX >= 2) ? 2 : 1);
-  if (a.d == 128) {
-    if (hpw == 4) return launch_one<128, 4>(a, st);
-    if (hpw == 2) return launch_one<128, 2>(a, st);
-    return launch_one<128, 1>(a, st);
-  }
-  if (hpw == 4) return launch_one<64, 4>(a, st);
-  if (hpw == 2) return launch_one<64, 2>(a, st);
-  return launch_one<64, 1>(a, st);
+  if (a.d == 128) return a.rowsum ? launch_d<128, true>(a, st) : launch_d<128, false>(a, st);
+  return a.rowsum ? launch_d<64, true>(a, st) : launch_d<64, false>(a, st);
 }
 
 size_t attn_workspace_bytes(const int B, const int Hq, const int N, const int d) {

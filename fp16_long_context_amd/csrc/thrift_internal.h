@@ -62,7 +62,8 @@ struct AttnArgs {
   float *lse;
   float *ws;  // partial state of every row after its FP16 blocks
   int B, Hq, Hkv, N, d, causal, out_dtype;
-  float c;  // fl32(sm_scale * log2 e)
+  int rowsum;  // 0: the row sum adds the unquantized p; 1: the weights P.V uses
+  float c;     // fl32(sm_scale * log2 e)
 };
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);

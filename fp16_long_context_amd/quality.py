@@ -28,12 +28,13 @@ import sys
 import time
 
 
-def errors(binding, torch, qz: dict, w, needles, frac: float) -> dict:
-    """err(frac) and err(0) against frac = 1, all rows and needle rows."""
+def errors(binding, torch, qz: dict, w, needles, frac: float, rowsum: str = "p") -> dict:
+    """err(frac) and err(0) against frac = 1, all rows and needle rows (the
+    frac = 1 reference is always the plain FP16 attention, rowsum "p")."""
     outs = {}
     for f in (1.0, frac, 0.0):
         idx, n16 = binding.select(qz["q16"], qz["k16"], f, True)
-        outs[f], _ = binding.attn_fwd(qz, idx, n16, True)
+        outs[f], _ = binding.attn_fwd(qz, idx, n16, True, rowsum="p" if f == 1.0 else rowsum)
         del idx, n16
     ref = outs[1.0]
     dev = ref.device

@@ -11,6 +11,8 @@
  *   thrift_quantize   FP16 copies of Q/K/V and their MXFP4 codes
  *   thrift_select     the block heuristic: FP16 and FP4 traversal lists
  *   thrift_attn_fwd   fused mixed-precision attention with one online softmax
+ *                     (thrift_attn_fwd_wsum: the same, normalised by the
+ *                     quantized weights)
  *
  * Conventions shared by every call:
  *   - Tensor pointers are DEVICE pointers owned and allocated by the caller;
@@ -145,8 +147,23 @@ int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, cons
                     const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
                     float *lse, void *workspace, size_t ws_bytes, void *stream);
 
-/* Bytes of device workspace thrift_attn_fwd needs for shape s (0 if s is
- * invalid): B * Hq * N/64 * (2 * 64 * (d/2 + 2) + 1) * 4. */
+/* thrift_attn_fwd under the other reading of the online-softmax row sum
+ * ("ThriftAttention: Selective Mixed Precision for Long-Context FP4
+ * Attention", abstract: both paths "merged via online softmax"; the pages do
+ * not say which weights the denominator adds): here l adds the weights the
+ * P.V products actually use, fp16(p) on FP16 tiles and the dequantized
+ * MXFP4 code of p on FP4 tiles, so every output row is a convex combination
+ * of V rows with exactly those weights (V = 1 gives O = 1).  On FP4 tiles the
+ * sum comes from one extra scaled MFMA against E2M1 ones instead of a VALU
+ * add per score.  Arguments, layouts, ownership, workspace and errors are
+ * those of thrift_attn_fwd; lse = (M + log2 l) ln 2 with this l. */
+int thrift_attn_fwd_wsum(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
+                         const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
+                         const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
+                         float *lse, void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of device workspace thrift_attn_fwd (and thrift_attn_fwd_wsum) needs
+ * for shape s (0 if s is invalid): B * Hq * N/64 * (2 * 64 * (d/2 + 2) + 1) * 4. */
 size_t thrift_attn_workspace_bytes(const thrift_shape *s);
 
 /* Static string naming a status code. */

@@ -54,8 +54,12 @@ def sel(L, s, frac=0.05, ptrs=None, ws=FAKE, wsb=1 << 40):
 
 
 def attn(L, s, out_dtype=2, ptrs=None, lse=None, sm=0.0, ws=FAKE, wsb=1 << 40):
+    """Both attention entry points validate alike; returns their common code."""
     ptrs = ptrs or [FAKE] * 12
-    return L.thrift_attn_fwd(ctypes.byref(s), sm, *ptrs[:11], ptrs[11], out_dtype, lse, ws, wsb, None)
+    codes = {fn(ctypes.byref(s), sm, *ptrs[:11], ptrs[11], out_dtype, lse, ws, wsb, None)
+             for fn in (L.thrift_attn_fwd, L.thrift_attn_fwd_wsum)}
+    assert len(codes) == 1, codes
+    return codes.pop()
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -77,6 +81,7 @@ def test_null_shape(L):
     assert L.thrift_quantize(None, 0, *[FAKE] * 12, None) == EINVAL
     assert L.thrift_select(None, 0.1, *[FAKE] * 4, FAKE, 1 << 40, None) == EINVAL
     assert L.thrift_attn_fwd(None, 0.0, *[FAKE] * 12, 2, None, FAKE, 1 << 40, None) == EINVAL
+    assert L.thrift_attn_fwd_wsum(None, 0.0, *[FAKE] * 12, 2, None, FAKE, 1 << 40, None) == EINVAL
     assert L.thrift_select_workspace_bytes(None) == 0 and L.thrift_list_entries(None) == 0
     assert L.thrift_attn_workspace_bytes(None) == 0
 

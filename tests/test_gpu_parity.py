@@ -35,17 +35,18 @@ def gpu_layout_to_oracle(qz):
     }
 
 
-def run_case(q, k, v, frac, causal=True, rows=None, label=""):
-    """Run both sides; assert the bit-exact parts; return the attention comparison."""
+def run_case(q, k, v, frac, causal=True, rows=None, label="", rowsum="p"):
+    """Run both sides; assert the bit-exact parts; return the attention comparison.
+    rowsum selects the row-sum reading on both sides ("p" or "weights")."""
     dtype = "fp16" if q.dtype == torch.float16 else "bf16"
     B, Hq, N, d = q.shape
-    say(f"[case] {label} B={B} Hq={Hq} Hkv={k.shape[1]} N={N} d={d} frac={frac} causal={causal} {dtype}")
+    say(f"[case] {label} B={B} Hq={Hq} Hkv={k.shape[1]} N={N} d={d} frac={frac} causal={causal} {dtype} rowsum={rowsum}")
     qz_o = oracle.quantize(synth.bits(q), synth.bits(k), synth.bits(v), dtype)
     sel_o = oracle.select(qz_o["q16"], qz_o["k16"], frac, causal)
     dev = torch.device("cuda:0")
     qz = binding.quantize(q.to(dev), k.to(dev), v.to(dev))
     idx, n16 = binding.select(qz["q16"], qz["k16"], frac, causal)
-    out, lse = binding.attn_fwd(qz, idx, n16, causal, want_lse=True)
+    out, lse = binding.attn_fwd(qz, idx, n16, causal, want_lse=True, rowsum=rowsum)
     torch.cuda.synchronize()
     g = gpu_layout_to_oracle(qz)
     for n in g:
@@ -53,7 +54,7 @@ def run_case(q, k, v, frac, causal=True, rows=None, label=""):
     assert np.array_equal(n16.cpu().numpy(), sel_o["n16"]), f"{label}: n16 differs"
     assert np.array_equal(idx.cpu().numpy(), sel_o["idx"]), f"{label}: idx differs"
     rows = oracle.all_rows(B, Hq, N) if rows is None else np.asarray(rows, dtype=np.int64)
-    res = oracle.attn_rows(qz_o, sel_o, rows, causal)
+    res = oracle.attn_rows(qz_o, sel_o, rows, causal, rowsum=rowsum)
     og = out.reshape(-1, d).cpu().numpy().astype(np.float64)[rows]
     lg = lse.reshape(-1).cpu().numpy().astype(np.float64)[rows]
     err = np.abs(og - res["out"]).max() / np.abs(res["out"]).max()
@@ -195,3 +196,58 @@ def test_single_fp16_block_lists(delta):
     err = np.abs(og - res["out"]).max() / np.abs(res["out"]).max()
     say(f"[case] offset {delta}: max|dO|/max|O| = {err:.3e}")
     assert err <= TOL
+
+
+# ------------------------------------------- row sum over the quantized weights
+
+
+def test_wsum_tiny_and_generators():
+    x = synth.generate("tiny")
+    run_case(x["q"], x["k"], x["v"], 0.05, label="tiny", rowsum="weights")
+    y = synth.generate("long_128k", N=1024)
+    run_case(y["q"], y["k"], y["v"], 0.05, label="rope@1k", rowsum="weights")
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.05, 1.0])
+def test_wsum_llama_shaped(frac):
+    x = synth.generate("llama8b_16k", N=1024)
+    run_case(x["q"], x["k"], x["v"], frac, label=f"llama8b@1k frac={frac}", rowsum="weights")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,dtype,frac", [
+    (2, 14, 2, 512, 128, True, "bf16", 0.05),
+    (1, 4, 2, 512, 64, True, "fp16", 0.3),
+    (1, 3, 3, 320, 128, False, "fp16", 0.3),
+    (1, 2, 1, 64, 128, True, "bf16", 0.05),
+])
+def test_wsum_shapes(B, Hq, Hkv, N, d, causal, dtype, frac):
+    q, k, v = synth.random_qkv(B, Hq, Hkv, N, d, dtype, seed=B * 1000 + N, scale=1.5)
+    run_case(q, k, v, frac, causal, label="shape", rowsum="weights")
+
+
+def test_wsum_constant_values_give_one():
+    # V = 1: the weights row sum makes every output exactly a sum of weights
+    # over itself; the GPU's fp32 sums of the same weights differ only in order
+    q, k, _ = synth.random_qkv(1, 8, 2, 2048, 128, "bf16", seed=53, scale=1.5)
+    v = torch.ones((1, 2, 2048, 128), dtype=torch.bfloat16)
+    dev = torch.device("cuda:0")
+    qz = binding.quantize(q.to(dev), k.to(dev), v.to(dev))
+    for frac in (0.0, 0.05, 1.0):
+        idx, n16 = binding.select(qz["q16"], qz["k16"], frac)
+        out, _ = binding.attn_fwd(qz, idx, n16, rowsum="weights")
+        err = (out - 1.0).abs().max().item()
+        say(f"[case] V=1 frac={frac}: max|O - 1| = {err:.3e}")
+        assert err < 1e-5
+
+
+def test_wsum_redo_walk_on_overflow():
+    q, k, v = synth.random_qkv(1, 4, 1, 512, 128, "fp16", seed=77)
+    k[0, 0, 200] = (12.0 * q[0, 0, 450].float()).to(q.dtype)
+    run_case(q, k, v, 0.0, label="redo walk", rowsum="weights")
+
+
+def test_wsum_full_size_sampled():
+    x = synth.generate("llama8b_16k")
+    w = x["w"]
+    rows = sample_rows(x, w.B, w.Hq, w.N, 40, 7)
+    run_case(x["q"], x["k"], x["v"], w.frac, rows=rows, label="llama8b_16k", rowsum="weights")
