@@ -810,10 +810,22 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   // KV-head-major order: the workgroups in flight at any time work on one
   // or two KV heads, whose FP16 K/V (128 N d bytes each) then stays in the
   // last-level cache while all their query heads and blocks read it.  Within
-  // a KV head, longest causal rows first.
-  const int kv = blockIdx.x / (nb * group), rem = blockIdx.x % (nb * group);
-  const int wi = rem / group;
-  const int b = kv / a.Hkv, hq = (kv % a.Hkv) * group + rem % group;
+  // a KV head, longest causal rows first; with the round-robin dispatch over
+  // the 8 XCDs, XCD x takes query blocks x, x+8, ... with all heads of the
+  // group, so the blocks the heads share (the first and diagonal blocks, and
+  // common picks) meet in one L2.
+  const int kv = blockIdx.x / (nb * group), rem0 = blockIdx.x % (nb * group);
+  // XCD (blockIdx % 8) takes every 8th query block with all heads of the group
+  int wi, hh;
+  if (nb % 8 == 0) {
+    const int x = rem0 % 8, t = rem0 / 8;  // t-th item of XCD x
+    hh = t % group;
+    wi = 8 * (t / group) + x;
+  } else {
+    wi = rem0 / group;
+    hh = rem0 % group;
+  }
+  const int b = kv / a.Hkv, hq = (kv % a.Hkv) * group + hh;
   const int bh = b * a.Hq + hq;
   const int i = a.causal ? nb - 1 - wi : wi;
   const int nv = a.causal ? i + 1 : nb;
