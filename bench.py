@@ -213,6 +213,7 @@ def main():
     t_q = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     t_s = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     t_a = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    t_as = sorted(e[2].elapsed_time(e[3]) for e in evs)
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), "
         f"quantize {t_q:.3f} select {t_s:.3f} attn {t_a:.3f} ms")
 
@@ -245,7 +246,8 @@ def main():
         "kernels": {
             "quantize_ms": round(t_q, 4), "quantize_GBps": round(quantize_bytes(w) / (t_q * 1e-3) / 1e9, 1),
             "select_ms": round(t_s, 4), "select_GBps": round(select_bytes(w) / (t_s * 1e-3) / 1e9, 1),
-            "attn_ms": round(t_a, 4), "attn_TFLOPs": round(achieved, 2), "hbm_peak_GBps": PEAK_HBM,
+            "attn_ms": round(t_a, 4), "attn_ms_median": round(t_as[len(t_as) // 2], 4),
+            "attn_ms_min": round(t_as[0], 4), "attn_TFLOPs": round(achieved, 2), "hbm_peak_GBps": PEAK_HBM,
         },
     }
     if not args.no_alt:
