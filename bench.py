@@ -23,6 +23,10 @@ Prints one JSON line:
   kernels    quantize / select / attention times and algorithmic GB/s;
   quality    planted-needle check: error of frac=0.05 and of frac=0 against
              frac=1 (all-FP16) output;
+  roofline_alu  the dominant kernel (attn_fwd_kernel, FP4 tiles) against
+             the bound it runs into, full-rate VALU issue: 5.5 issue slots per
+             FP4 score / its duration (HIP events the library records between
+             its kernels), peak 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz;
   alt_rowsum_weights  the attention call under the other row-sum reading
              (thrift_attn_fwd_wsum: normalised by the quantized weights, the
              FP4 row sums from one more MFMA), timed alone over the same
@@ -44,6 +48,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_F16 = 2516.6  # TFLOP/s, dense FP16 MFMA, MI355X
 PEAK_F4 = 10066.0  # TFLOP/s, dense MXFP4 MFMA, MI355X
 PEAK_HBM = 8000.0  # GB/s, MI355X HBM3E
+# full-rate wave64 VALU issue of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# (fp32 vector 157.3 TFLOP/s counts an fma as 2 and packed ops as 2 more)
+PEAK_VALU = 256 * 4 * 16 * 2.4e9 / 1e12  # T lane-ops/s
+# full-rate VALU issue slots per FP4 score: fma (s*c - M) 1, v_exp_f32 2 (half
+# rate), row-sum add 1, group max 1/2 (max3), FP4 convert 1 (half rate, 2 codes)
+VALU_SLOTS_PER_FP4_SCORE = 5.5
 METRIC = "attention TFLOPs/s at frac=0.05 + % of FP16/MXFP4 MFMA roofline, N=128K"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_long_128k_traffic.txt")
 ATTN_SRC = os.path.join(ROOT, "fp16_long_context_amd", "csrc", "attn_fwd.hip")
@@ -183,23 +193,21 @@ def main():
     aws = torch.empty(binding.attn_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d), dtype=torch.uint8, device=dev)
 
     def step(evs=None):
+        # evs: before quantize, before select, then the attention call's own
+        # four events (before, between and after its three kernels)
         if evs:
             evs[0].record()
         binding.quantize(q, k, v, out=qz)
         if evs:
             evs[1].record()
         binding.select(qz["q16"], qz["k16"], frac, True, workspace=ws, idx=idx, n16=n16)
-        if evs:
-            evs[2].record()
-        binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws)
-        if evs:
-            evs[3].record()
+        binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws, events=evs[2:6] if evs else None)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -212,8 +220,11 @@ def main():
     ms_step = e_start.elapsed_time(e_end) / args.steps
     t_q = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     t_s = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    t_a = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    t_as = sorted(e[2].elapsed_time(e[3]) for e in evs)
+    t_a = sum(e[2].elapsed_time(e[5]) for e in evs) / args.steps
+    t_as = sorted(e[2].elapsed_time(e[5]) for e in evs)
+    t_f16 = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    t_f4 = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
+    t_redo = sum(e[4].elapsed_time(e[5]) for e in evs) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), "
         f"quantize {t_q:.3f} select {t_s:.3f} attn {t_a:.3f} ms")
 
@@ -248,7 +259,16 @@ def main():
             "select_ms": round(t_s, 4), "select_GBps": round(select_bytes(w) / (t_s * 1e-3) / 1e9, 1),
             "attn_ms": round(t_a, 4), "attn_ms_median": round(t_as[len(t_as) // 2], 4),
             "attn_ms_min": round(t_as[0], 4), "attn_TFLOPs": round(achieved, 2), "hbm_peak_GBps": PEAK_HBM,
+            "attn_f16_kernel_ms": round(t_f16, 4), "attn_fwd_kernel_ms": round(t_f4, 4),
+            "attn_redo_kernel_ms": round(t_redo, 4),
         },
+        # the dominant kernel (FP4 tiles) against its own bound, the VALU:
+        # algorithmic work = the softmax's full-rate issue slots per FP4 score
+        "roofline_alu": {"bound": "alu", "kernel": "attn_fwd_kernel",
+                         "achieved": round(VALU_SLOTS_PER_FP4_SCORE * (F4 / (4 * w.d)) / (t_f4 * 1e-3) / 1e12, 2),
+                         "peak": round(PEAK_VALU, 2), "unit": "T VALU lane-ops/s",
+                         "frac": round(VALU_SLOTS_PER_FP4_SCORE * (F4 / (4 * w.d)) / (t_f4 * 1e-3) / 1e12 / PEAK_VALU, 4),
+                         "fp4_scores": F4 / (4 * w.d), "slots_per_score": VALU_SLOTS_PER_FP4_SCORE},
     }
     if not args.no_alt:
         # the same attention call normalised by the quantized weights

@@ -29,7 +29,8 @@ class Shape(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("thrift_quantize", "thrift_select_workspace_bytes", "thrift_list_entries", "thrift_select",
-           "thrift_attn_fwd", "thrift_attn_fwd_wsum", "thrift_attn_workspace_bytes", "thrift_status_str")
+           "thrift_attn_fwd", "thrift_attn_fwd_wsum", "thrift_attn_fwd_ex", "thrift_attn_workspace_bytes",
+           "thrift_status_str")
 
 
 def lib() -> ctypes.CDLL:
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
         for fn in (L.thrift_attn_fwd, L.thrift_attn_fwd_wsum):
             fn.argtypes = [SP, f32] + [P] * 11 + [P, i32, P, P, sz, P]
             fn.restype = i32
+        L.thrift_attn_fwd_ex.argtypes = [SP, f32] + [P] * 11 + [P, i32, P, P, sz, P, i32, P]
+        L.thrift_attn_fwd_ex.restype = i32
         L.thrift_attn_workspace_bytes.argtypes = [SP]
         L.thrift_attn_workspace_bytes.restype = sz
         L.thrift_status_str.argtypes = [i32]
@@ -161,11 +164,13 @@ def attn_workspace_bytes(B, Hq, Hkv, N, d, causal=True) -> int:
 
 def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True, sm_scale: float = 0.0,
              out_dtype=torch.float32, want_lse: bool = False, out=None, lse=None, workspace=None,
-             rowsum: str = "p"):
+             rowsum: str = "p", events=None):
     """Fused FP16/MXFP4 attention.  Returns (out [B,Hq,N,d], lse [B,Hq,N] or None).
     out, lse and the workspace (uint8, thrift_attn_workspace_bytes) may be preallocated.
     rowsum "p" (thrift_attn_fwd): the row sum adds the unquantized p;
-    "weights" (thrift_attn_fwd_wsum): it adds the weights the P.V products use."""
+    "weights" (thrift_attn_fwd_wsum): it adds the weights the P.V products use.
+    events: optional four torch.cuda.Event(enable_timing=True), recorded on the
+    current stream before, between and after the three kernels (thrift_attn_fwd_ex)."""
     if rowsum not in ("p", "weights"):
         raise ThriftError("rowsum must be 'p' or 'weights'")
     q16 = qz["q16"]
@@ -185,11 +190,19 @@ def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True
         raise ThriftError("unsupported shape")
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q16.device)
-    fn = L.thrift_attn_fwd if rowsum == "p" else L.thrift_attn_fwd_wsum
-    rc = fn(ctypes.byref(s), float(sm_scale),
-                           *[_ptr(qz[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
-                           _ptr(idx), _ptr(n16), _ptr(out), _DT[out.dtype], _ptr(lse), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(q16.device))
+    args = [ctypes.byref(s), float(sm_scale),
+            *[_ptr(qz[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
+            _ptr(idx), _ptr(n16), _ptr(out), _DT[out.dtype], _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q16.device)]
+    if events is None:
+        rc = (L.thrift_attn_fwd if rowsum == "p" else L.thrift_attn_fwd_wsum)(*args)
+    else:
+        if len(events) != 4:
+            raise ThriftError("events must hold four torch.cuda.Event")
+        for e in events:  # make sure each event exists on the device
+            e.record()
+        evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        rc = L.thrift_attn_fwd_ex(*args, 0 if rowsum == "p" else 1, evs)
     _check(rc, "thrift_attn_fwd")
     return out, lse
 

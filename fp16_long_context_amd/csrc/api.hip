@@ -100,7 +100,8 @@ size_t thrift_attn_workspace_bytes(const thrift_shape *s) {
 static int attn_fwd_common(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
                            const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
                            const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
-                           float *lse, void *workspace, size_t ws_bytes, void *stream, int rowsum) {
+                           float *lse, void *workspace, size_t ws_bytes, void *stream, int rowsum,
+                           void *const *events) {
   int rc = check_shape(s);
   if (rc != THRIFT_OK) return rc;
   if (out_dtype != THRIFT_F16 && out_dtype != THRIFT_BF16 && out_dtype != THRIFT_F32) return THRIFT_EINVAL;
@@ -122,7 +123,7 @@ static int attn_fwd_common(const thrift_shape *s, float sm_scale, const void *q1
   // score scale in log2 units, rounded once to fp32
   const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)s->d));
   a.c = (float)((double)sm * 1.4426950408889634074);
-  return launch_attn_fwd(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+  return launch_attn_fwd(a, (hipStream_t)stream, (hipEvent_t const *)events) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
 }
 
 int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
@@ -130,7 +131,7 @@ int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, cons
                     const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype, float *lse,
                     void *workspace, size_t ws_bytes, void *stream) {
   return attn_fwd_common(s, sm_scale, q16, k16, v16, q4, q4s, k4, k4s, v4, v4s, idx, n16, out, out_dtype, lse,
-                         workspace, ws_bytes, stream, 0);
+                         workspace, ws_bytes, stream, 0, nullptr);
 }
 
 int thrift_attn_fwd_wsum(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
@@ -138,7 +139,17 @@ int thrift_attn_fwd_wsum(const thrift_shape *s, float sm_scale, const void *q16,
                          const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
                          float *lse, void *workspace, size_t ws_bytes, void *stream) {
   return attn_fwd_common(s, sm_scale, q16, k16, v16, q4, q4s, k4, k4s, v4, v4s, idx, n16, out, out_dtype, lse,
-                         workspace, ws_bytes, stream, 1);
+                         workspace, ws_bytes, stream, 1, nullptr);
+}
+
+int thrift_attn_fwd_ex(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
+                       const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
+                       const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
+                       float *lse, void *workspace, size_t ws_bytes, void *stream, int rowsum,
+                       void *const *events) {
+  if (rowsum != 0 && rowsum != 1) return THRIFT_EINVAL;
+  return attn_fwd_common(s, sm_scale, q16, k16, v16, q4, q4s, k4, k4s, v4, v4s, idx, n16, out, out_dtype, lse,
+                         workspace, ws_bytes, stream, rowsum, events);
 }
 
 }  // extern "C"

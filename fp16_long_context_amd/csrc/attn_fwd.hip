@@ -1247,8 +1247,10 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   if (!flagged && head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
 }
 
+// ev (nullable): four caller-created events recorded on st before the FP16
+// kernel, between the kernels and after the redo kernel.
 template <int D, int HPW, bool W>
-static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
+static hipError_t launch_one(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {
   using T = Tile<D, HPW>;
   const int group = a.Hq / a.Hkv;
   const int chunks = (group + HPW - 1) / HPW;
@@ -1259,29 +1261,35 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t st) {
   e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           T::F4_LDS);
   if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          T::LDS);
+  if (e != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   hipLaunchKernelGGL((attn_f16_kernel<D, W>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(256), Tile16<D>::LDS, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   const dim3 grid4(nb * (unsigned)(a.B * a.Hkv * chunks));
   hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, W>), grid4, dim3(128 * HPW), T::F4_LDS, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          T::LDS);
-  if (e != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   hipLaunchKernelGGL((attn_redo_kernel<D, HPW, W>), grid4, dim3(128 * HPW), T::LDS, st, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev) e = hipEventRecord(ev[3], st);
+  return e;
 }
 
 template <int D, bool W>
-static hipError_t launch_d(const AttnArgs &a, hipStream_t st) {
+static hipError_t launch_d(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {
   // two heads of a GQA group per FP4 workgroup when the group has two
-  return (a.Hq / a.Hkv >= 2) ? launch_one<D, 2, W>(a, st) : launch_one<D, 1, W>(a, st);
+  return (a.Hq / a.Hkv >= 2) ? launch_one<D, 2, W>(a, st, ev) : launch_one<D, 1, W>(a, st, ev);
 }
 
-hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st) {
-  if (a.d == 128) return a.rowsum ? launch_d<128, true>(a, st) : launch_d<128, false>(a, st);
-  return a.rowsum ? launch_d<64, true>(a, st) : launch_d<64, false>(a, st);
+hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {
+  if (a.d == 128) return a.rowsum ? launch_d<128, true>(a, st, ev) : launch_d<128, false>(a, st, ev);
+  return a.rowsum ? launch_d<64, true>(a, st, ev) : launch_d<64, false>(a, st, ev);
 }
 
 size_t attn_workspace_bytes(const int B, const int Hq, const int N, const int d) {

@@ -68,7 +68,9 @@ struct AttnArgs {
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
-hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st);
+// ev: nullable, four events recorded before, between and after the three
+// attention kernels
+hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev = nullptr);
 // bytes of the attention workspace (partial state of every query row)
 size_t attn_workspace_bytes(int B, int Hq, int N, int d);
 

@@ -162,6 +162,19 @@ int thrift_attn_fwd_wsum(const thrift_shape *s, float sm_scale, const void *q16,
                          const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
                          float *lse, void *workspace, size_t ws_bytes, void *stream);
 
+/* thrift_attn_fwd (rowsum 0) or thrift_attn_fwd_wsum (rowsum 1) with an
+ * optional timing hook: events, when not NULL, points at four hipEvent_t
+ * the caller created (as void *); they are recorded on `stream` before the
+ * FP16-tile kernel, between it and the FP4-tile kernel, between that and the
+ * overflow-redo kernel, and after it, so the caller can time each kernel
+ * with hipEventElapsedTime.  Errors: those of thrift_attn_fwd, THRIFT_EINVAL
+ * for another rowsum, THRIFT_EHIP if an event cannot be recorded. */
+int thrift_attn_fwd_ex(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
+                       const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
+                       const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
+                       float *lse, void *workspace, size_t ws_bytes, void *stream, int rowsum,
+                       void *const *events);
+
 /* Bytes of device workspace thrift_attn_fwd (and thrift_attn_fwd_wsum) needs
  * for shape s (0 if s is invalid): B * Hq * N/64 * (2 * 64 * (d/2 + 2) + 1) * 4. */
 size_t thrift_attn_workspace_bytes(const thrift_shape *s);
