@@ -251,3 +251,24 @@ def test_wsum_full_size_sampled():
     w = x["w"]
     rows = sample_rows(x, w.B, w.Hq, w.N, 40, 7)
     run_case(x["q"], x["k"], x["v"], w.frac, rows=rows, label="llama8b_16k", rowsum="weights")
+
+
+def test_timing_hook_events_and_same_output():
+    # thrift_attn_fwd_ex with four events: the same output bits as
+    # thrift_attn_fwd, and the events bracket the three kernels in order
+    x = synth.generate("llama8b_16k", N=2048)
+    dev = torch.device("cuda:0")
+    qz = binding.quantize(*(x[n].to(dev) for n in ("q", "k", "v")))
+    idx, n16 = binding.select(qz["q16"], qz["k16"], 0.05)
+    plain, _ = binding.attn_fwd(qz, idx, n16)
+    for rowsum in ("p", "weights"):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        hooked, _ = binding.attn_fwd(qz, idx, n16, rowsum=rowsum, events=ev)
+        ref, _ = binding.attn_fwd(qz, idx, n16, rowsum=rowsum)
+        torch.cuda.synchronize()
+        assert torch.equal(hooked, ref)
+        if rowsum == "p":
+            assert torch.equal(hooked, plain)
+        t = [ev[0].elapsed_time(ev[i]) for i in (1, 2, 3)]
+        say(f"[case] timing hook {rowsum}: kernel ends at {t} ms")
+        assert 0.0 <= t[0] <= t[1] <= t[2]
