@@ -11,7 +11,9 @@
 //     two key halves are merged through LDS at the end and the partial state
 //     (unnormalised O^T, M, the lane's row-sum part) goes to the workspace.
 //   * attn_fwd_kernel: one workgroup per (batch, HPW query heads of one GQA
-//     group, query block i) starts from those partial states and walks, in
+//     group, query block i); HPW = 2 over the pairs of a group's heads and 1
+//     for the last head of an odd group.  It starts from those partial
+//     states and walks, in
 //     ascending order, every block that is on the FP4 list of at least one
 //     of its heads, staging the block's MXFP4 K/V once for all of them.  A
 //     wave owns 32 query rows of one head and computes the blocks on its own
@@ -516,14 +518,17 @@ __device__ __forceinline__ void tile_fp16(const uint8_t *st16, const uint8_t *qr
   }
 }
 
-// Work item of one GQA workgroup: query block i of the HPW heads of chunk
-// `chunk` of GQA group g in batch b (longest causal rows first).
+// Work item of one GQA workgroup: query block i of up to HPW heads of GQA
+// group g in batch b (longest causal rows first).  The launch covers heads
+// [a.hbase, a.hbase + a.hspan) of each group in chunks of hpw; this item
+// holds group heads h0 .. h0 + nh - 1 (nh < hpw only in a last, partial
+// chunk).
 struct WorkItem {
-  int i, b, g, chunk, nb, group, nv, nw;
+  int i, b, g, h0, nh, nb, group, nv, nw;
   __device__ __forceinline__ WorkItem(const AttnArgs &a, const int hpw) {
     nb = a.N / 64;
     group = a.Hq / a.Hkv;
-    const int chunks = (group + hpw - 1) / hpw;
+    const int chunks = (a.hspan + hpw - 1) / hpw;
     const int per_i = a.B * a.Hkv * chunks;
     const int wi = blockIdx.x / per_i;
     int rem = blockIdx.x % per_i;
@@ -531,7 +536,9 @@ struct WorkItem {
     b = rem / (a.Hkv * chunks);
     rem %= a.Hkv * chunks;
     g = rem / chunks;
-    chunk = rem % chunks;
+    const int chunk = rem % chunks;
+    h0 = a.hbase + chunk * hpw;
+    nh = min(hpw, a.hspan - chunk * hpw);
     nv = a.causal ? i + 1 : nb;
     nw = (nv + 31) / 32;
   }
@@ -951,8 +958,8 @@ __device__ __forceinline__ void build_masks(const AttnArgs &a, const WorkItem &w
   const int64_t per = a.causal ? (int64_t)w.nb * (w.nb + 1) / 2 : (int64_t)w.nb * w.nb;
   const int64_t roff = a.causal ? (int64_t)w.i * (w.i + 1) / 2 : (int64_t)w.i * w.nb;
   for (int h = 0; h < HPW; h++) {
-    const int hg = w.chunk * HPW + h;
-    if (hg >= w.group) break;
+    if (h >= w.nh) break;
+    const int hg = w.h0 + h;
     const int64_t bh = (int64_t)w.b * a.Hq + w.g * w.group + hg;
     const int cnt = a.n16[bh * w.nb + w.i];
     const int32_t *l16 = a.idx + bh * per + roff;
@@ -964,9 +971,10 @@ __device__ __forceinline__ void build_masks(const AttnArgs &a, const WorkItem &w
   __syncthreads();
 }
 
-// Redo flag of F4 workgroup `wg` in the workspace (after the partial state).
+// This launch's redo flags in the workspace (after the partial state),
+// indexed by FP4 workgroup.
 __device__ __forceinline__ int *redo_flags(const AttnArgs &a) {
-  return (int *)(a.ws + (size_t)a.B * a.Hq * (a.N / 64) * 2 * 64 * (a.d / 2 + 2));
+  return (int *)(a.ws + (size_t)a.B * a.Hq * (a.N / 64) * 2 * 64 * (a.d / 2 + 2)) + a.fbase;
 }
 
 // ---------------------------------------------------------------------------
@@ -985,12 +993,10 @@ __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = wave_u >> 1, qhalf = wave_u & 1;
-  const int hgrp = w.chunk * HPW + hl;
-  const bool head_ok = hgrp < w.group;
-  const int hq = w.g * w.group + (head_ok ? hgrp : 0);
+  const bool head_ok = hl < w.nh;
+  const int hq = w.g * w.group + w.h0 + (head_ok ? hl : 0);
   const int col = lane & 31, lh = lane >> 5;
-  const uint32_t head_bits =
-      (w.chunk * HPW + HPW <= w.group) ? ((1u << HPW) - 1) : ((1u << (w.group - w.chunk * HPW)) - 1);
+  const uint32_t head_bits = (1u << w.nh) - 1;
   uint32_t *mask = (uint32_t *)(smem + T::oMASK);
   build_masks<HPW>(a, w, mask);
   const int64_t qrow0 = ((int64_t)w.b * a.Hq + hq) * a.N + 64 * (int64_t)w.i + 32 * qhalf;
@@ -1077,13 +1083,12 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   uint32_t *imask = (uint32_t *)(smem + T::f4IMASK);  // blocks on every head's FP16 list
 
   const WorkItem w(a, HPW);
-  const int i = w.i, b = w.b, g = w.g, chunk = w.chunk, nb = w.nb, group = w.group, nv = w.nv, nw = w.nw;
+  const int i = w.i, b = w.b, g = w.g, nb = w.nb, group = w.group, nv = w.nv, nw = w.nw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = wave_u >> 1, qhalf = wave_u & 1;
-  const int hgrp = chunk * HPW + hl;
-  const bool head_ok = hgrp < group;
-  const int hq = g * group + (head_ok ? hgrp : 0);
+  const bool head_ok = hl < w.nh;
+  const int hq = g * group + w.h0 + (head_ok ? hl : 0);
   const int col = lane & 31, lh = lane >> 5;
 
   const int64_t qrow = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf + col;
@@ -1096,7 +1101,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   }
   // ---- FP16-list bitmask of each head of the workgroup
   build_masks<HPW>(a, w, mask);
-  const uint32_t head_bits = (chunk * HPW + HPW <= group) ? ((1u << HPW) - 1) : ((1u << (group - chunk * HPW)) - 1);
+  const uint32_t head_bits = (1u << w.nh) - 1;
   for (int e = tid; e < nw; e += NT) {
     uint32_t m = ~0u;
 #pragma unroll
@@ -1247,44 +1252,64 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   if (!flagged && head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
 }
 
-// ev (nullable): four caller-created events recorded on st before the FP16
-// kernel, between the kernels and after the redo kernel.
 template <int D, int HPW, bool W>
-static hipError_t launch_one(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {
+static hipError_t set_fp4_attrs() {
   using T = Tile<D, HPW>;
+  hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW, W>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, T::F4_LDS);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             T::LDS);
+}
+
+// The FP16 kernel over every (b, query head, query block); then the FP4
+// kernel over pairs of heads of each GQA group in two-head workgroups and,
+// for an odd group, its last head in one-head workgroups (no wave of a
+// two-head workgroup idles); then the redo kernels over the same grids.
+// ev (nullable): four caller-created events recorded on st before the FP16
+// kernel, between the kernels and after the redo kernels.
+template <int D, bool W>
+static hipError_t launch_d(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {
   const int group = a.Hq / a.Hkv;
-  const int chunks = (group + HPW - 1) / HPW;
+  const int pairs = group / 2, single = group % 2;
   const unsigned nb = (unsigned)(a.N / 64);
+  const unsigned per_head = nb * (unsigned)(a.B * a.Hkv);  // workgroups per head of a group
+  AttnArgs a2 = a, a1 = a;
+  a2.hbase = 0;
+  a2.hspan = 2 * pairs;
+  a2.fbase = 0;
+  a1.hbase = 2 * pairs;
+  a1.hspan = single;
+  a1.fbase = (int)(per_head * (unsigned)pairs);
+  const dim3 grid2(per_head * (unsigned)pairs), grid1(per_head);
   hipError_t e = hipFuncSetAttribute((const void *)attn_f16_kernel<D, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      Tile16<D>::LDS);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          T::F4_LDS);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          T::LDS);
-  if (e != hipSuccess) return e;
+  if (pairs && (e = set_fp4_attrs<D, 2, W>()) != hipSuccess) return e;
+  if (single && (e = set_fp4_attrs<D, 1, W>()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   hipLaunchKernelGGL((attn_f16_kernel<D, W>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(256), Tile16<D>::LDS, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-  const dim3 grid4(nb * (unsigned)(a.B * a.Hkv * chunks));
-  hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, W>), grid4, dim3(128 * HPW), T::F4_LDS, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (pairs) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 2, W>), grid2, dim3(256), (Tile<D, 2>::F4_LDS), st, a2);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (single) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 1, W>), grid1, dim3(128), (Tile<D, 1>::F4_LDS), st, a1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_redo_kernel<D, HPW, W>), grid4, dim3(128 * HPW), T::LDS, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (pairs) {
+    hipLaunchKernelGGL((attn_redo_kernel<D, 2, W>), grid2, dim3(256), (Tile<D, 2>::LDS), st, a2);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (single) {
+    hipLaunchKernelGGL((attn_redo_kernel<D, 1, W>), grid1, dim3(128), (Tile<D, 1>::LDS), st, a1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev) e = hipEventRecord(ev[3], st);
   return e;
-}
-
-template <int D, bool W>
-static hipError_t launch_d(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {
-  // two heads of a GQA group per FP4 workgroup when the group has two
-  return (a.Hq / a.Hkv >= 2) ? launch_one<D, 2, W>(a, st, ev) : launch_one<D, 1, W>(a, st, ev);
 }
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {

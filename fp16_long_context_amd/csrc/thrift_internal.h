@@ -64,6 +64,10 @@ struct AttnArgs {
   int B, Hq, Hkv, N, d, causal, out_dtype;
   int rowsum;  // 0: the row sum adds the unquantized p; 1: the weights P.V uses
   float c;     // fl32(sm_scale * log2 e)
+  // Set by the attention launcher for each FP4/redo launch: the launch
+  // covers heads [hbase, hbase + hspan) of every GQA group, and its
+  // workgroup w keeps its redo flag at index fbase + w.
+  int hbase = 0, hspan = 0, fbase = 0;
 };
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
