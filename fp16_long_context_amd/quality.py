@@ -11,13 +11,17 @@ benchmarks with trained models; here the planted-needle workloads stand in:
   needle, for the mixed fraction and for pure FP4 (frac = 0);
 * length_sweep(): the same at several sequence lengths of one generator;
 * attribution(): the gain of computing single blocks in FP16, against the
-  selection heuristic's block score and the exact attention mass.
+  selection heuristic's block score and the exact attention mass;
+* heuristics(): the output error when the FP16 blocks are picked by other
+  block scores (max-pooled, norm-weighted, exact block max) or at a block
+  size of 128, under the same budget rule, through caller-built lists.
 
 Everything runs through the library (quantize, select, attention); nothing
 here is an oracle.
 
     python -m fp16_long_context_amd.quality --sweep 4096,16384,65536,131072
     python -m fp16_long_context_amd.quality --attribution --workload llama8b_16k --N 4096
+    python -m fp16_long_context_amd.quality --heuristics --workload long_128k --N 16384
 """
 from __future__ import annotations
 
@@ -241,6 +245,175 @@ def attribution(workload: str = "llama8b_16k", N: int | None = None, frac: float
     return res
 
 
+def pooled_means(x16, rows: int = 64):
+    """fp32 means of `rows`-row blocks of [..., N, d] fp16: the exact fp64 sum
+    of the block, scaled and rounded to fp32 once (the selector's pooling)."""
+    N, d = x16.shape[-2], x16.shape[-1]
+    xd = x16.double().reshape(*x16.shape[:-2], N // rows, rows, d)
+    return (xd.sum(-2) * (1.0 / rows)).float()
+
+
+def sequential_scores(qbar, kbar):
+    """fp64 dot products of [..., nq, d] and [..., nk, d] fp32 means, summed
+    in channel order (each product of two fp32 values is exact in fp64, so
+    this matches an fma chain in that order bit for bit): [..., nq, nk]."""
+    import torch
+
+    qd, kd = qbar.double(), kbar.double()
+    s = torch.zeros(qd.shape[:-1] + (kd.shape[-2],), dtype=torch.float64, device=qd.device)
+    for c in range(qd.shape[-1]):
+        s = s + qd[..., :, c, None] * kd[..., None, :, c]
+    return s
+
+
+def select_mask(score, frac: float, causal: bool = True):
+    """FP16 blocks of every row block under the selector's budget rule, for
+    any block score [..., nb, nb]: with ppm = round(frac * 1e6), no FP16 blocks
+    at ppm = 0; else the first and diagonal blocks are forced and the
+    best-scoring others are added up to k = min(n_valid, max(|forced|,
+    ceil(ppm * n_valid / 1e6))) blocks in all, ties to the lower block index.
+    Returns a bool mask [..., nb, nb]."""
+    import torch
+
+    nb = score.shape[-1]
+    dev = score.device
+    ar = torch.arange(nb, device=dev)
+    i, j = ar[:, None], ar[None, :]
+    valid = (j <= i) if causal else torch.ones(nb, nb, dtype=torch.bool, device=dev)
+    ppm = int(math.floor(frac * 1e6 + 0.5))  # llround for frac >= 0
+    if ppm == 0:
+        return torch.zeros(score.shape, dtype=torch.bool, device=dev)
+    nv = valid.sum(-1)
+    forced = (j == 0) | (j == i)
+    nforced = forced.sum(-1)
+    k = torch.minimum(nv, torch.maximum(nforced, (ppm * nv + 999999) // 1000000))
+    key = score.double().masked_fill(~valid, float("-inf")).masked_fill(forced, float("inf"))
+    order = torch.sort(key, dim=-1, descending=True, stable=True).indices
+    rank = torch.empty_like(order)
+    rank.scatter_(-1, order, ar.expand_as(order).contiguous())
+    return (rank < k[:, None]) & valid
+
+
+def lists_from_mask(fp16, causal: bool = True):
+    """(idx, n16) in the library's list layout from a bool FP16 mask
+    [B, Hq, nb, nb]: per row block the FP16 blocks ascending, then the other
+    valid blocks ascending."""
+    import torch
+
+    B, Hq, nb, _ = fp16.shape
+    dev = fp16.device
+    ar = torch.arange(nb, device=dev)
+    valid = (ar[None, :] <= ar[:, None]) if causal else torch.ones(nb, nb, dtype=torch.bool, device=dev)
+    fp16 = fp16 & valid
+    skey = torch.where(valid, (~fp16).long() * nb + ar, 2 * nb + ar)
+    order = torch.argsort(skey, dim=-1)
+    idx = order[:, :, valid.sum(-1)[:, None] > ar[None, :]].to(torch.int32).reshape(-1).contiguous()
+    return idx, fp16.sum(-1).to(torch.int32).contiguous()
+
+
+def expand_mask(fp16_big, factor: int):
+    """An FP16 mask over blocks of factor*64 rows expanded to 64-row blocks
+    (causally clipped by the list builder)."""
+    return fp16_big.repeat_interleave(factor, dim=-2).repeat_interleave(factor, dim=-1)
+
+
+def heuristics(workload: str = "long_128k", N: int | None = None, frac: float = 0.05, log=None) -> list:
+    """Output error of the mixed path when the FP16 blocks come from other
+    block scores, each under the selector's budget rule (first and diagonal
+    blocks forced), run through the library with caller-built lists:
+
+    * pooled_mean: the selector's own score (q-block mean . k-block mean); its
+      lists are checked to equal the library's selection;
+    * max_pooled: max over the key rows r of block j of (q-block mean . k_r),
+      so a single strong key is not averaged away;
+    * norm_weighted: block means weighted by each row's L2 norm;
+    * block_max: the block's largest exact score (needs the full QK^T; a
+      comparator, not a cheap heuristic);
+    * pooled_mean_128: the selector's score and rule on 128-row blocks, each
+      selected 128-block pair expanded to its four 64-row tile pairs.
+
+    Each entry: err and needle-row err against the all-FP16 output, and the
+    share of causal tiles computed in FP16.
+    """
+    import torch
+
+    from . import binding, synth
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    x = synth.generate(workload, N=N)
+    w = x["w"]
+    B, Hq, Hkv, Nn, d = w.B, w.Hq, w.Hkv, w.N, w.d
+    nb = Nn // 64
+    grp = Hq // Hkv
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    qz = binding.quantize(q, k, v)
+    del q, k, v
+    ws = torch.empty(binding.attn_workspace_bytes(B, Hq, Hkv, Nn, d), dtype=torch.uint8, device=dev)
+    rows = torch.tensor([(b * Hq + hq) * Nn + t for (b, kvh, hq, p, t) in x["needles"]], device=dev)
+    idx, n16 = binding.select(qz["q16"], qz["k16"], 1.0, True)
+    ref, _ = binding.attn_fwd(qz, idx, n16, True, workspace=ws)
+    r2 = ref.reshape(-1, d)[rows]
+    ref_norm, r2_norm = torch.linalg.vector_norm(ref).item(), torch.linalg.vector_norm(r2).item()
+    tiles = B * Hq * nb * (nb + 1) // 2
+    out = []
+
+    def run(name, idx, n16):
+        o, _ = binding.attn_fwd(qz, idx, n16, True, workspace=ws)
+        r = {"heuristic": name, "workload": workload, "N": Nn, "frac": frac,
+             "err": round(torch.linalg.vector_norm(o - ref).item() / ref_norm, 6),
+             "needle_err": round(torch.linalg.vector_norm(o.reshape(-1, d)[rows] - r2).item() / r2_norm, 6),
+             "fp16_tile_share": round(float(n16.sum()) / tiles, 5)}
+        if log:
+            log(json.dumps(r))
+        out.append(r)
+
+    lib_idx, lib_n16 = binding.select(qz["q16"], qz["k16"], frac, True)
+    run("library_select", lib_idx, lib_n16)
+    idx0, n160 = binding.select(qz["q16"], qz["k16"], 0.0, True)
+    run("fp4_only", idx0, n160)
+    del idx0, n160
+
+    q16, k16 = qz["q16"], qz["k16"]
+    kq = lambda t: t.repeat_interleave(grp, dim=1)  # noqa: E731  KV head of each query head
+    # the selector's score, recomputed here: its lists must be the library's
+    qbar, kbar = pooled_means(q16), pooled_means(k16)
+    score = sequential_scores(qbar, kq(kbar))
+    idx, n16 = lists_from_mask(select_mask(score, frac))
+    same = bool(torch.equal(idx, lib_idx) and torch.equal(n16, lib_n16))
+    run("pooled_mean", idx, n16)
+    out[-1]["equals_library"] = same
+    del lib_idx, lib_n16, score
+    # max-pooled and exact block max, one head at a time
+    mp = torch.empty((B, Hq, nb, nb), dtype=torch.float64, device=dev)
+    bm = torch.empty((B, Hq, nb, nb), dtype=torch.float64, device=dev)
+    for b in range(B):
+        for h in range(Hq):
+            kh = k16[b, h // grp].float()
+            mp[b, h] = torch.matmul(qbar[b, h].double(), kh.double().t().contiguous()).view(nb, nb, 64).amax(-1)
+            for r0 in range(0, Nn, 4096):
+                r1 = min(Nn, r0 + 4096)
+                s_ = torch.matmul(q16[b, h, r0:r1].float(), kh.t().contiguous())
+                bm[b, h, r0 // 64:r1 // 64] = s_.view((r1 - r0) // 64, 64, nb, 64).amax(dim=(1, 3)).double()
+    run("max_pooled", *lists_from_mask(select_mask(mp, frac)))
+    run("block_max", *lists_from_mask(select_mask(bm, frac)))
+    del mp, bm
+    # norm-weighted means
+    def nw_means(x16):
+        xf = x16.float().view(*x16.shape[:-2], nb, 64, d)
+        wgt = torch.linalg.vector_norm(xf, dim=-1, keepdim=True)
+        return ((xf * wgt).sum(-2) / wgt.sum(-2).clamp_min(1e-30)).float()
+
+    run("norm_weighted", *lists_from_mask(select_mask(sequential_scores(nw_means(q16), kq(nw_means(k16))), frac)))
+    # 128-row blocks
+    if nb % 2 == 0:
+        s128 = sequential_scores(pooled_means(q16, 128), kq(pooled_means(k16, 128)))
+        run("pooled_mean_128", *lists_from_mask(expand_mask(select_mask(s128, frac), 2)))
+    for r in out:
+        r["seconds"] = round(time.perf_counter() - t0, 2)
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--sweep", default="4096,8192,16384,32768,65536,131072",
@@ -249,7 +422,9 @@ def main(argv=None) -> int:
     ap.add_argument("--frac", type=float, default=None)
     ap.add_argument("--attribution", action="store_true",
                     help="block-level error attribution instead of the length sweep")
-    ap.add_argument("--N", type=int, default=None, help="sequence length of the attribution run")
+    ap.add_argument("--heuristics", action="store_true",
+                    help="output error under other block scores and at block size 128")
+    ap.add_argument("--N", type=int, default=None, help="sequence length of the attribution or heuristics run")
     args = ap.parse_args(argv)
     Ns = [int(s) for s in args.sweep.split(",") if s]
     if any(n <= 0 or n % 64 for n in Ns) or (args.N is not None and (args.N <= 0 or args.N % 64)):
@@ -258,6 +433,8 @@ def main(argv=None) -> int:
     log = lambda s: print(s, flush=True)  # noqa: E731
     if args.attribution:
         attribution(args.workload, args.N, 0.05 if args.frac is None else args.frac, log=log)
+    elif args.heuristics:
+        heuristics(args.workload, args.N, 0.05 if args.frac is None else args.frac, log=log)
     else:
         length_sweep(Ns, args.workload, args.frac, log=log)
     return 0

@@ -30,3 +30,21 @@ def test_attribution_small():
     for key in ("capture_score", "capture_mass", "capture_blockmax", "capture_select"):
         assert r[key] <= 1.0 + 1e-9
     assert 0.0 < r["concentration"] <= 1.0 + 1e-9
+
+
+@pytest.mark.parametrize("workload", ["long_128k", "llama8b_16k"])
+def test_heuristics_small(workload):
+    rows = quality.heuristics(workload, N=2048, log=lambda s: print(s, flush=True))
+    by = {r["heuristic"]: r for r in rows}
+    assert list(by) == ["library_select", "fp4_only", "pooled_mean", "max_pooled", "block_max",
+                        "norm_weighted", "pooled_mean_128"]
+    # the study's list builder reproduces the library's own selection exactly
+    assert by["pooled_mean"]["equals_library"]
+    assert by["pooled_mean"]["err"] == by["library_select"]["err"]
+    assert by["fp4_only"]["fp16_tile_share"] == 0.0
+    # the same budget rule at 64-row blocks gives every score the same FP16 share
+    for name in ("max_pooled", "block_max", "norm_weighted"):
+        assert by[name]["fp16_tile_share"] == by["library_select"]["fp16_tile_share"]
+    for r in rows:
+        assert math.isfinite(r["err"]) and 0.0 < r["err"] < 1.0, r
+        assert math.isfinite(r["needle_err"]) and 0.0 < r["needle_err"] < 1.0, r
