@@ -83,7 +83,8 @@ def test_llama_shaped_2k_sampled():
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,dtype,frac", [
-    (2, 14, 2, 512, 128, True, "bf16", 0.05),   # GQA group of 7: a partial head chunk
+    (2, 14, 2, 512, 128, True, "bf16", 0.05),   # GQA group of 7: three head pairs + one lone head
+    (1, 10, 2, 640, 64, True, "bf16", 0.2),     # GQA group of 5, d = 64
     (1, 4, 2, 512, 64, True, "fp16", 0.3),      # group of 2, d = 64
     (1, 3, 3, 320, 128, False, "fp16", 0.3),    # non-causal, 5 blocks
     (1, 2, 1, 64, 128, True, "bf16", 0.05),     # a single block
