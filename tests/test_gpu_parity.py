@@ -145,6 +145,38 @@ def test_full_size_workloads_sampled(name):
     run_case(x["q"], x["k"], x["v"], w.frac, rows=rows, label=name)
 
 
+def test_frac_sweep_64k_sampled():
+    """The 64K configuration's FP16 fractions on the same tensors: codes once,
+    then at every fraction the lists bit-exact and attention on sampled rows
+    within the bar (the fraction moves work between the two kernels)."""
+    x = synth.generate("sweep_64k")
+    w = x["w"]
+    say(f"[case] sweep_64k B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} d={w.d} fracs 0..1")
+    qz_o = oracle.quantize(synth.bits(x["q"]), synth.bits(x["k"]), synth.bits(x["v"]), "bf16")
+    dev = torch.device("cuda:0")
+    qz = binding.quantize(x["q"].to(dev), x["k"].to(dev), x["v"].to(dev))
+    g = gpu_layout_to_oracle(qz)
+    for n in g:
+        assert np.array_equal(g[n], qz_o[n]), f"sweep_64k: {n} differs"
+    del g
+    rows = sample_rows(x, w.B, w.Hq, w.N, 24, 11)
+    for frac in (0.0, 0.01, 0.05, 0.2, 1.0):
+        sel_o = oracle.select(qz_o["q16"], qz_o["k16"], frac, True)
+        idx, n16 = binding.select(qz["q16"], qz["k16"], frac, True)
+        out, lse = binding.attn_fwd(qz, idx, n16, True, want_lse=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(n16.cpu().numpy(), sel_o["n16"]), f"frac {frac}: n16 differs"
+        assert np.array_equal(idx.cpu().numpy(), sel_o["idx"]), f"frac {frac}: idx differs"
+        res = oracle.attn_rows(qz_o, sel_o, rows, True)
+        og = out.reshape(-1, w.d).cpu().numpy().astype(np.float64)[rows]
+        lg = lse.reshape(-1).cpu().numpy().astype(np.float64)[rows]
+        err = np.abs(og - res["out"]).max() / np.abs(res["out"]).max()
+        lerr = np.abs(lg - res["lse"]).max()
+        say(f"[case] sweep_64k frac {frac}: max|dO|/max|O| = {err:.3e}, max|dLSE| = {lerr:.3e}")
+        assert err <= TOL and lerr <= 1e-3, (frac, err, lerr)
+        del idx, n16, out, lse
+
+
 def test_maximum_blocks():
     # N = 64 * 8192, the largest supported block count
     q, k, v = synth.random_qkv(1, 2, 1, 64 * 8192, 64, "fp16", seed=77)
