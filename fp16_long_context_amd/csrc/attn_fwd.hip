@@ -702,8 +702,7 @@ template <int D>
 struct Tile16 {
   static constexpr int FP16_BYTES = Tile<D, 1>::FP16_BYTES;
   static constexpr int SLOTS = THRIFT_F16_SLOTS;      // ring of FP16 tiles: SLOTS - 1 loads in flight
-  static constexpr int oQ16 = SLOTS * FP16_BYTES;
-  static constexpr int LDS = oQ16 + 64 * D * 2;       // Q16 of the block's 64 rows
+  static constexpr int LDS = SLOTS * FP16_BYTES;      // Q stays in registers
   static_assert(Partial<D>::FIELDS * 64 * 4 * 2 <= SLOTS * FP16_BYTES, "merge buffer fits in the slots");
 };
 
@@ -754,14 +753,14 @@ __device__ __forceinline__ void softmax_half(float16v &s, float16v (&acc)[CB], f
 }
 
 // One 32-key half (keys 32 kh + 0..31) of an FP16 tile for one wave: S^T from
-// FP16 K and Q (K rows fed so that register r holds key 16(r/8) + 8 lh + r%8),
-// P rounded to fp16, O^T += V^T P^T with FP16 V.
+// FP16 K (LDS; rows fed so that register r holds key 16(r/8) + 8 lh + r%8) and
+// the lane's Q row (registers), P rounded to fp16, O^T += V^T P^T with FP16 V.
 template <int D, bool MASK, bool W>
-__device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const uint8_t *qrow16, const int kh,
+__device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const half8 (&qreg)[D / 16], const int kh,
                                                float16v (&acc)[D / 32], float &M, float &l_part, const float c,
                                                const int col, const int lh, const int qpos) {
   using T = Tile<D, 1>;
-  constexpr int KS = D / 16, CB = D / 32, CPR = D / 8;
+  constexpr int KS = D / 16, CB = D / 32;
   // A-operand row rho reads key 16(rho/16) + 8((rho/4)%2) + 4((rho/8)%2) + rho%4
   // of the half (bits 2 and 3 of rho swapped)
   const int key = 32 * kh + (col & 0x13) + ((col & 4) << 1) + ((col & 8) >> 1);
@@ -779,7 +778,7 @@ __device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const uint8_
 #pragma unroll
     for (int u = 0; u < 2; u++) {
       const int chunk = 2 * (kk + u) + lh;
-      qb[u] = __builtin_bit_cast(half8, *(const int4v *)(qrow16 + 16 * (chunk ^ (col & (CPR - 1)))));
+      qb[u] = qreg[kk + u];
       ka[u] = __builtin_bit_cast(half8, *(const int4v *)(krow + 16 * (chunk ^ sw)));
     }
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qb[0], s0, 0, 0, 0);
@@ -842,9 +841,16 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   const int col = lane & 31, lh = lane >> 5;
   const int qpos = 32 * qhalf + col;
   const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf;
-  uint8_t *q16w = smem + Tile16<D>::oQ16 + (size_t)qhalf * 32 * D * 2;
-  if (kh == 0) stage_q16<D>(a, qrow0, q16w, lane);
-  const uint8_t *qrow16 = q16w + col * (2 * D);
+  // This lane's Q row (query qrow0 + col) in registers, as the B operand of
+  // the QK MFMAs: k-step kk takes channels 16 kk + 8 lh + 0..7.  Q is used
+  // by every tile of the walk; reading it from LDS each time would be a
+  // third of the kernel's LDS operand traffic.
+  half8 qreg[D / 16];
+  {
+    const uint16_t *qr = a.q16 + (qrow0 + col) * D + 8 * lh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; kk++) qreg[kk] = __builtin_bit_cast(half8, *(const int4v *)(qr + 16 * kk));
+  }
 
   const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
   const int64_t roff = a.causal ? (int64_t)i * (i + 1) / 2 : (int64_t)i * nb;
@@ -905,15 +911,15 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   // diagonal block is the last valid one): one unmasked body, no branches.
   for (int e = 0; e + 1 < cnt; e++)
     ring_step(e, [&](const uint8_t *st16, int) {
-      tile_fp16_half<D, false, W>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+      tile_fp16_half<D, false, W>(st16, qreg, kh, acc, M, l_part, a.c, col, lh, qpos);
     });
   if (cnt > 0)
     ring_step(cnt - 1, [&](const uint8_t *st16, int jc) {
       if (a.causal && jc == i) {
         // the upper key half of the diagonal has no valid key for the lower rows
-        if (!(kh == 1 && qhalf == 0)) tile_fp16_half<D, true, W>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+        if (!(kh == 1 && qhalf == 0)) tile_fp16_half<D, true, W>(st16, qreg, kh, acc, M, l_part, a.c, col, lh, qpos);
       } else {
-        tile_fp16_half<D, false, W>(st16, qrow16, kh, acc, M, l_part, a.c, col, lh, qpos);
+        tile_fp16_half<D, false, W>(st16, qreg, kh, acc, M, l_part, a.c, col, lh, qpos);
       }
     });
   // Merge the two key halves of each row (lane by lane: the same lane of the
