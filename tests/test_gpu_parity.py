@@ -196,6 +196,18 @@ def test_redo_walk_on_overflow():
     run_case(q, k, v, 0.0, label="redo walk")
 
 
+@pytest.mark.parametrize("rowsum", ["p", "weights"])
+def test_redo_walk_odd_group(rowsum):
+    """A GQA group of 3: heads 0-1 run in two-head FP4 workgroups and head 2
+    in the one-head launch, whose redo flags sit after the pairs'.  Overflow
+    keys planted for head 2 and for head 0 (different query blocks) must be
+    recomputed by the redo kernel of their own launch."""
+    q, k, v = synth.random_qkv(1, 3, 1, 512, 128, "fp16", seed=91)
+    k[0, 0, 200] = (12.0 * q[0, 2, 450].float()).to(q.dtype)  # head 2 (lone head), query block 7
+    k[0, 0, 70] = (12.0 * q[0, 0, 330].float()).to(q.dtype)   # head 0 (pair), query block 5
+    run_case(q, k, v, 0.0, label="redo walk, group of 3", rowsum=rowsum)
+
+
 @pytest.mark.parametrize("delta", [0, 5, 15])
 def test_single_fp16_block_lists(delta):
     """Lists that are not the selection's (one FP16 block per row block, at
