@@ -99,10 +99,15 @@ __device__ __forceinline__ int swz_k4(int key) {  // K4 rows: D/32 chunks
   if (D == 128) return (((key >> 1) ^ (key >> 2)) & 1) | (((key >> 5) & 1) << 1);
   return (key >> 5) & 1;
 }
+// K16 rows (D/8 chunks) are read in two patterns: the FP16 kernel's half
+// tiles (16 lanes vary key bits 0-3) and the redo walk's permuted full tiles
+// (16 lanes vary key bits 0, 1, 2 and 5).  Taking bit 3 ^ bit 5 into the map
+// makes it one-to-one on both sets of bits at D = 128.
 template <int D>
-__device__ __forceinline__ int swz_k16(int key) {  // K16 rows: D/8 chunks
-  if (D == 128) return (key & 3) | (((key >> 5) & 1) << 2) | (((key >> 2) & 1) << 3);
-  return ((key >> 1) & 1) | (((key >> 2) & 1) << 1) | (((key >> 5) & 1) << 2);
+__device__ __forceinline__ int swz_k16(int key) {
+  const int b35 = ((key >> 3) ^ (key >> 5)) & 1;
+  if (D == 128) return (key & 3) | (b35 << 2) | (((key >> 2) & 1) << 3);
+  return ((key >> 1) & 1) | (((key >> 2) & 1) << 1) | (b35 << 2);
 }
 __device__ __forceinline__ int swz_v16(int ch) { return (ch ^ (ch >> 3)) & 7; }       // V16 rows: 8 chunks
 __device__ __forceinline__ int swz_v4(int ch) { return ((ch >> 2) ^ (ch >> 3)) & 1; }  // V4 rows: 2 chunks
