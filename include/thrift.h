@@ -165,9 +165,10 @@ int thrift_attn_fwd_wsum(const thrift_shape *s, float sm_scale, const void *q16,
 /* thrift_attn_fwd (rowsum 0) or thrift_attn_fwd_wsum (rowsum 1) with an
  * optional timing hook: events, when not NULL, points at four hipEvent_t
  * the caller created (as void *); they are recorded on `stream` before the
- * FP16-tile kernel, between it and the FP4-tile kernel, between that and the
- * overflow-redo kernel, and after it, so the caller can time each kernel
- * with hipEventElapsedTime.  Errors: those of thrift_attn_fwd, THRIFT_EINVAL
+ * FP16-tile kernel, between it and the FP4-tile kernel launches (two for a
+ * GQA group of odd size: its head pairs, then its last head), between those
+ * and the overflow-redo launches, and after them, so the caller can time
+ * each phase with hipEventElapsedTime.  Errors: those of thrift_attn_fwd, THRIFT_EINVAL
  * for another rowsum, THRIFT_EHIP if an event cannot be recorded. */
 int thrift_attn_fwd_ex(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
                        const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
