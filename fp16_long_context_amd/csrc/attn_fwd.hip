@@ -799,6 +799,10 @@ __device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const half8 
 #pragma unroll
     for (int t = 0; t < 8; t++) pb[u][t] = (_Float16)s0[8 * u + t];
   const uint8_t *vt = st16 + T::oV16;
+  // The P.V MFMAs issue at raised wave priority: a wave that reaches them
+  // gets them into the matrix pipe ahead of the other wave's softmax work,
+  // so it reaches the end-of-tile barrier (and the next tile's loads) sooner.
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) {
     const int ch = 32 * cb + col;
@@ -809,6 +813,7 @@ __device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const half8 
       acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb[u], acc[cb], 0, 0, 0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D, bool W>
