@@ -851,16 +851,6 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   const int col = lane & 31, lh = lane >> 5;
   const int qpos = 32 * qhalf + col;
   const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * a.N + 64 * (int64_t)i + 32 * qhalf;
-  // This lane's Q row (query qrow0 + col) in registers, as the B operand of
-  // the QK MFMAs: k-step kk takes channels 16 kk + 8 lh + 0..7.  Q is used
-  // by every tile of the walk; reading it from LDS each time would be a
-  // third of the kernel's LDS operand traffic.
-  half8 qreg[D / 16];
-  {
-    const uint16_t *qr = a.q16 + (qrow0 + col) * D + 8 * lh;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; kk++) qreg[kk] = __builtin_bit_cast(half8, *(const int4v *)(qr + 16 * kk));
-  }
 
   const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
   const int64_t roff = a.causal ? (int64_t)i * (i + 1) / 2 : (int64_t)i * nb;
@@ -869,6 +859,22 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   typedef const __attribute__((address_space(4))) int32_t cint;
   cint *l16 = (cint *)(a.idx + (int64_t)bh * per + roff);
   const int cnt = min(max(((cint *)a.n16)[(int64_t)bh * nb + i], 0), nv);
+  // This lane's Q row (query qrow0 + col) in registers, as the B operand of
+  // the QK MFMAs: k-step kk takes channels 16 kk + 8 lh + 0..7.  Q is used
+  // by every tile of the walk; reading it from LDS each time would be a
+  // third of the kernel's LDS operand traffic.  A row block without FP16
+  // blocks (cnt == 0, wave-uniform) loads nothing.
+  half8 qreg[D / 16];
+  if (cnt > 0) {
+    const uint16_t *qr = a.q16 + (qrow0 + col) * D + 8 * lh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; kk++) qreg[kk] = __builtin_bit_cast(half8, *(const int4v *)(qr + 16 * kk));
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < D / 16; kk++)
+#pragma unroll
+      for (int t = 0; t < 8; t++) qreg[kk][t] = (_Float16)0.0f;
+  }
   // list entry e as a wave-uniform block index; an entry outside [0, nv)
   // (not produced by the selection) is clamped into it, so every access
   // stays inside this KV head's arrays
