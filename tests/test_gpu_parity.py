@@ -177,6 +177,29 @@ def test_frac_sweep_64k_sampled():
         del idx, n16, out, lse
 
 
+def test_attention_composer_and_sm_scale():
+    """binding.attention (quantize -> select -> attention in one call) with a
+    non-default softmax scale: equal to the three calls made one by one, and
+    within the bar of the oracle at the same scale."""
+    q, k, v = synth.random_qkv(1, 4, 2, 384, 64, "bf16", seed=17, scale=1.5)
+    dev = torch.device("cuda:0")
+    sm = 0.2
+    say("[case] attention() B=1 Hq=4 Hkv=2 N=384 d=64 bf16 frac=0.1 sm_scale=0.2")
+    out = binding.attention(q.to(dev), k.to(dev), v.to(dev), frac=0.1, sm_scale=sm)
+    qz = binding.quantize(q.to(dev), k.to(dev), v.to(dev))
+    idx, n16 = binding.select(qz["q16"], qz["k16"], 0.1, True)
+    out2, _ = binding.attn_fwd(qz, idx, n16, True, sm)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    qz_o = oracle.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "bf16")
+    sel_o = oracle.select(qz_o["q16"], qz_o["k16"], 0.1, True)
+    res = oracle.attn_rows(qz_o, sel_o, oracle.all_rows(1, 4, 384), True, sm_scale=sm)
+    og = out.reshape(-1, 64).cpu().numpy().astype(np.float64)
+    err = np.abs(og - res["out"]).max() / np.abs(res["out"]).max()
+    say(f"[case] attention(): max|dO|/max|O| = {err:.3e}")
+    assert err <= TOL
+
+
 def test_maximum_blocks():
     # N = 64 * 8192, the largest supported block count
     q, k, v = synth.random_qkv(1, 2, 1, 64 * 8192, 64, "fp16", seed=77)
