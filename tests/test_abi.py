@@ -152,3 +152,11 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.float16)
     with pytest.raises(binding.ThriftError):
         binding.quantize(q, q, q)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    # no fallback: a missing library is an error, not a silent CPU path
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "SO_PATH", str(tmp_path / "libthrift.so"))
+    with pytest.raises(binding.ThriftError):
+        binding.lib()
