@@ -105,18 +105,36 @@ def alloc_quantized(B, Hq, Hkv, N, d, device) -> dict:
     }
 
 
+def _check_quantized(r: dict, B, Hq, Hkv, N, d) -> None:
+    """Every buffer of a quantize output dict has the shape and dtype
+    alloc_quantized gives it (the C ABI sees bare pointers, so this is the
+    only place a wrong buffer can be caught before the kernels touch it)."""
+    want = alloc_quantized(B, Hq, Hkv, N, d, "meta")
+    for n, t in want.items():
+        if n not in r:
+            raise ThriftError(f"quantized buffer {n} missing")
+        x = r[n]
+        if not isinstance(x, torch.Tensor) or tuple(x.shape) != tuple(t.shape) or x.dtype != t.dtype:
+            got = (tuple(x.shape), x.dtype) if isinstance(x, torch.Tensor) else type(x)
+            raise ThriftError(f"quantized buffer {n} must be {tuple(t.shape)} {t.dtype}; got {got}")
+
+
 def quantize(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: dict | None = None) -> dict:
     """FP16 copies and MXFP4 codes of q [B,Hq,N,d], k/v [B,Hkv,N,d] (fp16 or bf16).
     Layouts as in include/thrift.h (v16/v4/v4s are tile-major).  `out` may
     hold preallocated buffers from alloc_quantized."""
-    _need_gpu(q, k, v)
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
         raise ThriftError("q, k, v must share dtype fp16 or bf16")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ThriftError("q, k, v must be 4-D [B,H,N,d]")
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ThriftError(f"k and v must be [B,Hkv,N,d] = [{B},Hkv,{N},{d}]; got {tuple(k.shape)}, {tuple(v.shape)}")
     dev = q.device
     r = alloc_quantized(B, Hq, Hkv, N, d, dev) if out is None else out
-    _need_gpu(*r.values())
+    _check_quantized(r, B, Hq, Hkv, N, d)
+    _need_gpu(q, k, v, *r.values())
     s = make_shape(B, Hq, Hkv, N, d)
     rc = lib().thrift_quantize(ctypes.byref(s), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v),
                                *[_ptr(r[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
@@ -134,9 +152,12 @@ def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = Tru
            n16=None):
     """Traversal lists: idx (int32, per-row FP16 list then FP4 list) and n16 [B,Hq,nb].
     idx, n16 and the workspace may be preallocated."""
-    _need_gpu(q16, k16)
+    if q16.dim() != 4 or k16.dim() != 4 or q16.dtype != torch.float16 or k16.dtype != torch.float16:
+        raise ThriftError("q16 and k16 must be 4-D fp16 tensors")
     B, Hq, N, d = q16.shape
     Hkv = k16.shape[1]
+    if tuple(k16.shape) != (B, Hkv, N, d):
+        raise ThriftError(f"k16 must be [B,Hkv,N,d] = [{B},Hkv,{N},{d}]; got {tuple(k16.shape)}")
     s = make_shape(B, Hq, Hkv, N, d, causal)
     L = lib()
     ents = int(L.thrift_list_entries(ctypes.byref(s)))
@@ -151,6 +172,7 @@ def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = Tru
         raise ThriftError("idx/n16 buffers too small or not int32")
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q16.device)
+    _need_gpu(q16, k16, idx, n16, workspace)
     rc = L.thrift_select(ctypes.byref(s), float(frac), _ptr(q16), _ptr(k16), _ptr(idx), _ptr(n16), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(q16.device))
     _check(rc, "thrift_select")
@@ -174,22 +196,34 @@ def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True
     if rowsum not in ("p", "weights"):
         raise ThriftError("rowsum must be 'p' or 'weights'")
     q16 = qz["q16"]
+    if q16.dim() != 4 or qz["k16"].dim() != 4:
+        raise ThriftError("q16/k16 must be 4-D")
     B, Hq, N, d = q16.shape
     Hkv = qz["k16"].shape[1]
-    _need_gpu(*qz.values(), idx, n16)
+    _check_quantized(qz, B, Hq, Hkv, N, d)
+    s = make_shape(B, Hq, Hkv, N, d, causal)
+    L = lib()
+    ents = int(L.thrift_list_entries(ctypes.byref(s)))
+    wsb = int(L.thrift_attn_workspace_bytes(ctypes.byref(s)))
+    if ents <= 0 or wsb <= 0:
+        raise ThriftError("unsupported shape")
+    if idx.dtype != torch.int32 or n16.dtype != torch.int32:
+        raise ThriftError("idx and n16 must be int32")
+    if idx.numel() < ents or n16.numel() < B * Hq * (N // 64):
+        raise ThriftError(f"idx needs {ents} entries and n16 {B * Hq * (N // 64)}; "
+                          f"got {idx.numel()} and {n16.numel()}")
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=out_dtype, device=q16.device)
-    if out.shape != (B, Hq, N, d) or out.dtype not in _DT:
+    if tuple(out.shape) != (B, Hq, N, d) or out.dtype not in _DT:
         raise ThriftError("out must be [B,Hq,N,d] fp32/fp16/bf16")
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q16.device)
-    s = make_shape(B, Hq, Hkv, N, d, causal)
-    L = lib()
-    wsb = int(L.thrift_attn_workspace_bytes(ctypes.byref(s)))
-    if wsb <= 0:
-        raise ThriftError("unsupported shape")
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.numel() < B * Hq * N:
+            raise ThriftError(f"lse must be fp32 with at least {B * Hq * N} elements")
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q16.device)
+    _need_gpu(*qz.values(), idx, n16, out, workspace, *([lse] if lse is not None else []))
     args = [ctypes.byref(s), float(sm_scale),
             *[_ptr(qz[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
             _ptr(idx), _ptr(n16), _ptr(out), _DT[out.dtype], _ptr(lse), _ptr(workspace),

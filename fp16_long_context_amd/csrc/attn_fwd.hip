@@ -876,11 +876,11 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
       for (int t = 0; t < 8; t++) qreg[kk][t] = (_Float16)0.0f;
   }
   // list entry e as a wave-uniform block index; an entry outside [0, nv)
-  // (not produced by the selection) is clamped into it, so every access
-  // stays inside this KV head's arrays
+  // (not produced by the selection) becomes -1 and is skipped: no load, no
+  // tile, so every access stays inside this KV head's arrays
   auto entry = [&](int e) {
     const int j = l16[e];
-    return min(max(j, 0), nv - 1);
+    return ((unsigned)j < (unsigned)nv) ? j : -1;
   };
   const Loader<D, 4> ld(a, b, hq / group, wave_u, lane);
 
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   // at the end of an entry keeps the newer entries' loads in flight.
   constexpr int R = Tile16<D>::SLOTS;
   constexpr int LPT = Loader<D, 4>::NG16;  // load instructions per tile and wave
-  int jq[R];                                // blocks of entries e .. e + R - 1 (-1: none)
+  int jq[R];                                // blocks of entries e .. e + R - 1 (-1: none or skipped)
 #pragma unroll
   for (int q = 0; q < R; q++) jq[q] = (q < cnt) ? entry(q) : -1;
 #pragma unroll
@@ -923,14 +923,17 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
     for (int q = 0; q < R - 1; q++) jq[q] = jq[q + 1];
     jq[R - 1] = (e + R < cnt) ? entry(e + R) : -1;
   };
-  // Entries before the last are never the diagonal (the list ascends and the
-  // diagonal block is the last valid one): one unmasked body, no branches.
+  // The list holds distinct blocks in ascending order, so entries before the
+  // last are never the diagonal block (the last valid one): one unmasked
+  // body in the loop; the last entry takes the masked body if it is the
+  // diagonal.  jc is wave-uniform (a scalar branch); -1 marks a skipped entry.
   for (int e = 0; e + 1 < cnt; e++)
-    ring_step(e, [&](const uint8_t *st16, int) {
-      tile_fp16_half<D, false, W>(st16, qreg, kh, acc, M, l_part, a.c, col, lh, qpos);
+    ring_step(e, [&](const uint8_t *st16, int jc) {
+      if (jc >= 0) tile_fp16_half<D, false, W>(st16, qreg, kh, acc, M, l_part, a.c, col, lh, qpos);
     });
   if (cnt > 0)
     ring_step(cnt - 1, [&](const uint8_t *st16, int jc) {
+      if (jc < 0) return;
       if (a.causal && jc == i) {
         // the upper key half of the diagonal has no valid key for the lower rows
         if (!(kh == 1 && qhalf == 0)) tile_fp16_half<D, true, W>(st16, qreg, kh, acc, M, l_part, a.c, col, lh, qpos);
@@ -983,7 +986,8 @@ __device__ __forceinline__ void build_masks(const AttnArgs &a, const WorkItem &w
     if (h >= w.nh) break;
     const int hg = w.h0 + h;
     const int64_t bh = (int64_t)w.b * a.Hq + w.g * w.group + hg;
-    const int cnt = a.n16[bh * w.nb + w.i];
+    // at most the row's n_valid entries (the FP16 kernel reads the same ones)
+    const int cnt = min(max(a.n16[bh * w.nb + w.i], 0), w.nv);
     const int32_t *l16 = a.idx + bh * per + roff;
     for (int e = tid; e < cnt; e += NT) {
       const int j = l16[e];

@@ -64,7 +64,8 @@ typedef struct {
 
 /*
  * Step 1 -- quantize (the block-scaled 4-bit operands of the FP4 path and the
- * FP16 operands of the FP16 path; the abstract's "block-scaled quantisation").
+ * FP16 operands of the FP16 path; the abstract names block-scaled 4-bit
+ * quantisation as the prior art it builds on).
  *
  * in_dtype: THRIFT_F16 or THRIFT_BF16 for q, k, v.
  * Inputs (row-major): q [B,Hq,N,d], k and v [B,Hkv,N,d].
@@ -92,8 +93,9 @@ size_t thrift_select_workspace_bytes(const thrift_shape *s);
 int64_t thrift_list_entries(const thrift_shape *s);
 
 /*
- * Step 2 -- select (the abstract's "heuristic rapidly selects a small number
- * of important query-key block pairs for FP16").
+ * Step 2 -- select ("ThriftAttention: Selective Mixed Precision for
+ * Long-Context FP4 Attention", abstract: a fast heuristic marks the few
+ * important query-key block pairs that stay in FP16).
  *
  * Heuristic: each 64-row block of q16 (per query head) and k16 (per KV head)
  * is mean-pooled (exact sum, one rounding to fp32); a block pair (i, j) is
@@ -118,9 +120,9 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
                   int32_t *n16, void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * Step 3 -- fused mixed-precision attention (the abstract's "selected blocks
- * are computed in FP16 and the remaining blocks in FP4, with both paths
- * merged via online softmax into a single output").
+ * Step 3 -- fused mixed-precision attention (same abstract: the marked
+ * blocks run in FP16, every other block in 4-bit, and one online softmax
+ * combines the two into a single output).
  *
  * For query row t of (b, h) in block i, every valid key (causal: key <= t)
  * of a block on the row's FP16 list is scored in FP16 (fp32 accumulation)
@@ -134,8 +136,10 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
  *   out = acc / l;  lse = (M + log2 l) * ln 2 (natural-log LSE of the scaled
  *   scores).
  * out [B,Hq,N,d] of out_dtype (THRIFT_F32, THRIFT_F16 or THRIFT_BF16);
- * lse [B,Hq,N] fp32, may be NULL.  idx/n16 must come from thrift_select with
- * the same shape (list entries outside [0, n_valid) are skipped).
+ * lse [B,Hq,N] fp32, may be NULL.  idx/n16 come from thrift_select with the
+ * same shape, or follow its layout: each row's FP16 list holds distinct
+ * blocks in ascending order; an entry outside [0, n_valid) is skipped, and
+ * an n16 above n_valid counts as n_valid.
  * workspace: device buffer of at least thrift_attn_workspace_bytes(s) bytes,
  * 16-byte aligned, owned by the caller; on return it holds each row's
  * partial softmax state after its FP16 blocks (no meaning for the caller).
@@ -149,7 +153,7 @@ int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, cons
 
 /* thrift_attn_fwd under the other reading of the online-softmax row sum
  * ("ThriftAttention: Selective Mixed Precision for Long-Context FP4
- * Attention", abstract: both paths "merged via online softmax"; the pages do
+ * Attention", abstract: one online softmax merges both paths; the pages do
  * not say which weights the denominator adds): here l adds the weights the
  * P.V products actually use, fp16(p) on FP16 tiles and the dequantized
  * MXFP4 code of p on FP4 tiles, so every output row is a convex combination

@@ -160,3 +160,68 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "SO_PATH", str(tmp_path / "libthrift.so"))
     with pytest.raises(binding.ThriftError):
         binding.lib()
+
+
+# ---- the binding checks every buffer's shape before anything reaches the C ABI
+# (CPU tensors: a wrong shape must be reported as such, ahead of the device check)
+
+
+def _cpu_qkv(B=1, Hq=4, Hkv=2, N=128, d=64):
+    import torch
+
+    q = torch.zeros(B, Hq, N, d, dtype=torch.float16)
+    k = torch.zeros(B, Hkv, N, d, dtype=torch.float16)
+    return q, k, k.clone()
+
+
+def test_binding_rejects_mismatched_kv_shapes():
+    import torch
+
+    q, k, v = _cpu_qkv()
+    with pytest.raises(binding.ThriftError, match="k and v must be"):
+        binding.quantize(q, k[:, :, :64], v)
+    with pytest.raises(binding.ThriftError, match="k and v must be"):
+        binding.quantize(q, k, torch.zeros(1, 2, 128, 32, dtype=torch.float16))
+    with pytest.raises(binding.ThriftError, match="k16 must be"):
+        binding.select(q, k[:, :, :, :32].contiguous(), 0.05)
+
+
+def test_binding_rejects_wrong_quantized_buffers():
+    import torch
+
+    q, k, v = _cpu_qkv()
+    out = binding.alloc_quantized(1, 4, 2, 128, 64, "cpu")
+    out["v4s"] = torch.empty(1, 2, 2, 64, 1, dtype=torch.uint8)  # one scale per 64 tokens: too small
+    with pytest.raises(binding.ThriftError, match="quantized buffer v4s"):
+        binding.quantize(q, k, v, out=out)
+    out = binding.alloc_quantized(1, 4, 2, 128, 64, "cpu")
+    del out["k4"]
+    with pytest.raises(binding.ThriftError, match="quantized buffer k4 missing"):
+        binding.quantize(q, k, v, out=out)
+
+
+def test_binding_rejects_short_lists_and_outputs():
+    import torch
+
+    qz = binding.alloc_quantized(1, 4, 2, 128, 64, "cpu")
+    ents = 4 * 2 * 3 // 2  # nb = 2: 3 entries per head
+    idx = torch.zeros(ents, dtype=torch.int32)
+    n16 = torch.zeros(1, 4, 2, dtype=torch.int32)
+    with pytest.raises(binding.ThriftError, match="idx needs"):
+        binding.attn_fwd(qz, idx[:-1], n16)
+    with pytest.raises(binding.ThriftError, match="idx needs"):
+        binding.attn_fwd(qz, idx, n16[:, :, :1])
+    with pytest.raises(binding.ThriftError, match="int32"):
+        binding.attn_fwd(qz, idx.long(), n16)
+    with pytest.raises(binding.ThriftError, match="lse must be"):
+        binding.attn_fwd(qz, idx, n16, lse=torch.zeros(4 * 128 - 1))
+    with pytest.raises(binding.ThriftError, match="out must be"):
+        binding.attn_fwd(qz, idx, n16, out=torch.zeros(1, 4, 128, 32))
+    bad = dict(qz)
+    bad["q4"] = torch.empty(1, 4, 128, 16, dtype=torch.uint8)
+    with pytest.raises(binding.ThriftError, match="quantized buffer q4"):
+        binding.attn_fwd(bad, idx, n16)
+    # shapes right, tensors on the CPU: the device check is what fails
+    with pytest.raises(binding.ThriftError, match="on a GPU"):
+        binding.attn_fwd(qz, idx, n16)
+
