@@ -104,6 +104,35 @@ def test_rope_and_heavy_tail_generators():
     run_case(y["q"], y["k"], y["v"], 0.05, label="heavy@512")
 
 
+@pytest.mark.parametrize("frac", [0.1, 0.2, 0.5])
+def test_select_ties_at_the_cutoff(frac):
+    """Key blocks that differ only by a tiny step in one channel: their block
+    scores agree in fp32 (often) and in fp64 (when the step is the same), so
+    the cut-off falls among tied blocks.  The lists must still equal the
+    oracle's (fp64 score descending, lower block index first)."""
+    g = np.random.default_rng(5)
+    B, H, N, d = 1, 2, 2048, 128
+    nb = N // 64
+    q = g.standard_normal((B, H, N, d))
+    q[..., 0] = 2.0 ** -8  # pooled Q mean of channel 0 is exactly 2^-8
+    r = g.standard_normal(d)
+    r[0] = 1.0
+    k = np.broadcast_to(r, (B, H, N, d)).copy()  # every key row the same
+    m = g.integers(0, 4, size=(H, nb))  # block j: one row's channel 0 up by m * 2^-10
+    for h in range(H):
+        for j in range(nb):
+            k[0, h, 64 * j, 0] += m[h, j] * 2.0 ** -10
+    q16 = torch.from_numpy(q.astype(np.float16))
+    k16 = torch.from_numpy(k.astype(np.float16))
+    say(f"[case] select ties B={B} H={H} N={N} d={d} frac={frac}")
+    sel_o = oracle.select(synth.bits(q16), synth.bits(k16), frac, True)
+    dev = torch.device("cuda:0")
+    idx, n16 = binding.select(q16.to(dev), k16.to(dev), frac, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(n16.cpu().numpy(), sel_o["n16"])
+    assert np.array_equal(idx.cpu().numpy(), sel_o["idx"])
+
+
 def test_output_dtypes_and_determinism():
     x = synth.generate("llama8b_16k", N=1024)
     dev = torch.device("cuda:0")
