@@ -29,6 +29,7 @@ class Shape(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("thrift_quantize", "thrift_select_workspace_bytes", "thrift_list_entries", "thrift_select",
+           "thrift_select_noalloc",
            "thrift_attn_fwd", "thrift_attn_fwd_wsum", "thrift_attn_fwd_ex", "thrift_attn_workspace_bytes",
            "thrift_status_str")
 
@@ -51,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.thrift_list_entries.restype = i64
         L.thrift_select.argtypes = [SP, f64, P, P, P, P, P, sz, P]
         L.thrift_select.restype = i32
+        L.thrift_select_noalloc.argtypes = [SP, f64, P, P, P, P, P]
+        L.thrift_select_noalloc.restype = i32
         for fn in (L.thrift_attn_fwd, L.thrift_attn_fwd_wsum):
             fn.argtypes = [SP, f32] + [P] * 11 + [P, i32, P, P, sz, P]
             fn.restype = i32
@@ -176,6 +179,34 @@ def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = Tru
     rc = L.thrift_select(ctypes.byref(s), float(frac), _ptr(q16), _ptr(k16), _ptr(idx), _ptr(n16), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(q16.device))
     _check(rc, "thrift_select")
+    return idx, n16
+
+
+def select_noalloc(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = True, idx=None, n16=None):
+    """thrift_select_noalloc: the lists of select() with the pooled means in the
+    library's static device array (no workspace; pass idx and n16 to allocate
+    nothing here either).  Calls that overlap on one GPU race."""
+    if q16.dim() != 4 or k16.dim() != 4 or q16.dtype != torch.float16 or k16.dtype != torch.float16:
+        raise ThriftError("q16 and k16 must be 4-D fp16 tensors")
+    B, Hq, N, d = q16.shape
+    Hkv = k16.shape[1]
+    if tuple(k16.shape) != (B, Hkv, N, d):
+        raise ThriftError(f"k16 must be [B,Hkv,N,d] = [{B},Hkv,{N},{d}]; got {tuple(k16.shape)}")
+    s = make_shape(B, Hq, Hkv, N, d, causal)
+    L = lib()
+    ents = int(L.thrift_list_entries(ctypes.byref(s)))
+    if ents <= 0:
+        raise ThriftError("unsupported shape")
+    if idx is None:
+        idx = torch.empty(ents, dtype=torch.int32, device=q16.device)
+    if n16 is None:
+        n16 = torch.empty((B, Hq, N // 64), dtype=torch.int32, device=q16.device)
+    if idx.numel() < ents or n16.numel() < B * Hq * (N // 64) or idx.dtype != torch.int32 or n16.dtype != torch.int32:
+        raise ThriftError("idx/n16 buffers too small or not int32")
+    _need_gpu(q16, k16, idx, n16)
+    rc = L.thrift_select_noalloc(ctypes.byref(s), float(frac), _ptr(q16), _ptr(k16), _ptr(idx), _ptr(n16),
+                                 _stream(q16.device))
+    _check(rc, "thrift_select_noalloc")
     return idx, n16
 
 

@@ -92,6 +92,25 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
   return launch_select(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
 }
 
+int thrift_select_noalloc(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx,
+                          int32_t *n16, void *stream) {
+  int rc = check_shape(s);
+  if (rc != THRIFT_OK) return rc;
+  if (!(frac >= 0.0 && frac <= 1.0)) return THRIFT_EINVAL;  // also rejects NaN
+  const void *ptrs[] = {q16, k16, idx, n16};
+  for (const void *p : ptrs)
+    if (!aligned_ok(p)) return THRIFT_EINVAL;
+  // the pooled means must fit the library's static scratch array
+  if (thrift_select_workspace_bytes(s) > kSelectScratchBytes) return THRIFT_EWORKSPACE;
+  SelectArgs a;
+  a.q16 = (const uint16_t *)q16; a.k16 = (const uint16_t *)k16;
+  a.idx = idx; a.n16 = n16;
+  a.qbar = nullptr; a.kbarT = nullptr;  // set by the launcher
+  a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
+  a.ppm = (int64_t)llround(frac * 1e6);
+  return launch_select_scratch(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
 size_t thrift_attn_workspace_bytes(const thrift_shape *s) {
   if (check_shape(s) != THRIFT_OK) return 0;
   return attn_workspace_bytes(s->B, s->Hq, s->N, s->d);

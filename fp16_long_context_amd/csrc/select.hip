@@ -25,6 +25,8 @@
 // (the rounding is monotone), so only blocks whose fp32 score equals the
 // cut-off need their fp64 scores, which the select kernel recomputes with
 // the same chain.
+#include <mutex>
+
 #include "thrift_internal.h"
 
 namespace thrift {
@@ -447,6 +449,45 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t st) {
                        a.d);
   }
   return a.d == 64 ? launch_select_d<64>(a, st) : launch_select_d<128>(a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Selection without a caller workspace: the pooled means live in `scratch`,
+// a static device array (one copy per GPU, held until the process ends).
+// Host code never passes the array's name to a kernel (in host code it is a
+// stand-in, not a device address): the first call on each device looks up
+// the array's device address with hipGetSymbolAddress, with that device
+// current, and every call uses that pointer.  Calls on one GPU share the
+// array, so calls that overlap in time on one GPU race; each call rewrites
+// every pooled mean it reads, so nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[kSelectScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t launch_select_scratch(SelectArgs a, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *ptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void *p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev] = p;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  a.qbar = (float *)ptr;
+  a.kbarT = (float *)ptr + (size_t)a.B * a.Hq * (a.N / 64) * a.d;
+  return launch_select(a, st);
 }
 
 }  // namespace thrift

@@ -72,6 +72,11 @@ struct AttnArgs {
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
+// Bytes of the static device array that holds the pooled means for
+// launch_select_scratch (which ignores a.qbar / a.kbarT and points them into
+// that array); callers check 4 * nb * d * B * (Hq + Hkv) against it first.
+constexpr size_t kSelectScratchBytes = (size_t)64 << 20;
+hipError_t launch_select_scratch(SelectArgs a, hipStream_t st);
 // ev: nullable, four events recorded before, between and after the three
 // attention kernels
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev = nullptr);

@@ -120,6 +120,22 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
                   int32_t *n16, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * thrift_select for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same lists, bit for bit, with no workspace argument.  The pooled means
+ * go to a static device array inside the library (64 MiB per GPU, held
+ * until the process ends); the call itself allocates nothing.  Limit:
+ * thrift_select_workspace_bytes(s) = 4 * nb * d * B * (Hq + Hkv) must not
+ * exceed 64 MiB (e.g. B = 1, Hq = 32, Hkv = 8, d = 128 up to N = 209664),
+ * else THRIFT_EWORKSPACE and nothing is launched.  Every call on one GPU
+ * shares that array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialized by the caller.
+ * Errors: those of thrift_select, THRIFT_EWORKSPACE beyond the limit.
+ */
+int thrift_select_noalloc(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx,
+                          int32_t *n16, void *stream);
+
+/*
  * Step 3 -- fused mixed-precision attention (same abstract: the marked
  * blocks run in FP16, every other block in 4-bit, and one online softmax
  * combines the two into a single output).

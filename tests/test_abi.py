@@ -53,6 +53,11 @@ def sel(L, s, frac=0.05, ptrs=None, ws=FAKE, wsb=1 << 40):
     return L.thrift_select(ctypes.byref(s), frac, *ptrs, ws, wsb, None)
 
 
+def sel_noalloc(L, s, frac=0.05, ptrs=None):
+    ptrs = ptrs or [FAKE] * 4
+    return L.thrift_select_noalloc(ctypes.byref(s), frac, *ptrs, None)
+
+
 def attn(L, s, out_dtype=2, ptrs=None, lse=None, sm=0.0, ws=FAKE, wsb=1 << 40):
     """Both attention entry points validate alike; returns their common code."""
     ptrs = ptrs or [FAKE] * 12
@@ -74,6 +79,7 @@ def test_bad_shapes(L, kw, code):
     s = shape(**kw)
     assert quant(L, s) == code
     assert sel(L, s) == code
+    assert sel_noalloc(L, s) == code
     assert attn(L, s) == code
     assert L.thrift_select_workspace_bytes(ctypes.byref(s)) == 0
     assert L.thrift_attn_workspace_bytes(ctypes.byref(s)) == 0
@@ -99,6 +105,7 @@ def test_null_and_misaligned_pointers(L, slot):
         assert attn(L, s, ptrs=p) == EINVAL
         if slot < 4:
             assert sel(L, s, ptrs=p[:4]) == EINVAL
+            assert sel_noalloc(L, s, ptrs=p[:4]) == EINVAL
     assert attn(L, s, lse=ctypes.c_void_p(0x10004)) == EINVAL
 
 
@@ -107,6 +114,7 @@ def test_bad_values(L):
     assert quant(L, s, dtype=2) == EINVAL and quant(L, s, dtype=-1) == EINVAL
     for f in (-0.01, 1.0001, math.nan, math.inf):
         assert sel(L, s, frac=f) == EINVAL
+        assert sel_noalloc(L, s, frac=f) == EINVAL
     assert attn(L, s, out_dtype=3) == EINVAL
     assert attn(L, s, sm=math.nan) == EINVAL and attn(L, s, sm=math.inf) == EINVAL
 
@@ -225,3 +233,14 @@ def test_binding_rejects_short_lists_and_outputs():
     with pytest.raises(binding.ThriftError, match="on a GPU"):
         binding.attn_fwd(qz, idx, n16)
 
+
+def test_noalloc_select_size_limit(L):
+    # the pooled means (4 nb d B (Hq + Hkv) bytes) must fit the library's
+    # 64 MiB static array: the 128K Llama-shaped layer fits, 8 more query
+    # heads do not; beyond the limit nothing is launched
+    assert L.thrift_select_noalloc(None, 0.05, *[FAKE] * 4, None) == EINVAL
+    fits = shape(B=1, Hq=32, Hkv=8, N=131072, d=128)
+    assert L.thrift_select_workspace_bytes(ctypes.byref(fits)) <= 64 << 20
+    too_big = shape(B=2, Hq=32, Hkv=8, N=131072, d=128)
+    assert L.thrift_select_workspace_bytes(ctypes.byref(too_big)) > 64 << 20
+    assert sel_noalloc(L, too_big) == EWS
