@@ -15,6 +15,10 @@ Parity status per function:
                                 search, closed forms)
   pool, select                  pinned (numpy means, brute-force subset search,
                                 list invariants, a worked example)
+  normw_pool, select(score=...) pinned (exactly representable inputs against
+                                numpy; brute-force scores on tiny inputs; a
+                                dominant key row for max-pooled; equal-norm rows
+                                reduce norm-weighted to the pooled mean)
   attn_rows                     pinned (frac=1 against textbook softmax
                                 attention, FP4-exact inputs against textbook
                                 attention, closed forms, split-merge);
@@ -67,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_list_entries.restype = i64
         L.oracle_select.argtypes = [i32] * 6 + [f64] + [P] * 7
         L.oracle_select.restype = i32
+        L.oracle_select_kind.argtypes = [i32] * 7 + [f64] + [P] * 7
+        L.oracle_select_kind.restype = i32
+        L.oracle_normw_pool.argtypes = [P, i64, i32, i32, P]
+        L.oracle_normw_pool.restype = None
         L.oracle_attn_rows.argtypes = [i32] * 6 + [f32] + [P] * 9 + [P, P, P, i64, P, P, P, P, P, P, i32]
         L.oracle_attn_rows.restype = i32
         _lib = L
@@ -137,8 +145,23 @@ def list_entries(B, Hq, N, causal) -> int:
     return int(lib().oracle_list_entries(B, Hq, N, int(causal)))
 
 
-def select(q16, k16, frac: float, causal: bool = True) -> dict:
-    """Block heuristic: pooled means, scores and the FP16/FP4 traversal lists."""
+SCORES = {"pooled_mean": 0, "max_pooled": 1, "norm_weighted": 2, "block_max": 3}
+
+
+def normw_pool(x16: np.ndarray) -> np.ndarray:
+    """Norm-weighted means of 64-row blocks (rows weighed by their L2 norms)."""
+    x = _c(x16, np.uint16)
+    B, H, N, d = x.shape
+    out = np.empty((B, H, N // 64, d), np.float32)
+    lib().oracle_normw_pool(_p(x), B * H, N, d, _p(out))
+    return out
+
+
+def select(q16, k16, frac: float, causal: bool = True, score: str = "pooled_mean") -> dict:
+    """Block heuristic: block means, scores and the FP16/FP4 traversal lists.
+    score: "pooled_mean" (the library's default), "max_pooled",
+    "norm_weighted" or "block_max" (the heuristic variants; same budget rule).
+    qbar/kbar hold the pooled means (norm-weighted means for "norm_weighted")."""
     q, k = _c(q16, np.uint16), _c(k16, np.uint16)
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -149,8 +172,8 @@ def select(q16, k16, frac: float, causal: bool = True) -> dict:
     qbar = np.empty((B, Hq, nb, d), np.float32)
     kbar = np.empty((B, Hkv, nb, d), np.float32)
     scores = np.full(E, np.nan, np.float64)
-    rc = lib().oracle_select(B, Hq, Hkv, N, d, int(causal), float(frac), _p(q), _p(k), _p(idx), _p(n16),
-                             _p(qbar), _p(kbar), _p(scores))
+    rc = lib().oracle_select_kind(SCORES[score], B, Hq, Hkv, N, d, int(causal), float(frac), _p(q), _p(k),
+                                  _p(idx), _p(n16), _p(qbar), _p(kbar), _p(scores))
     if rc != 0:
         raise ValueError("oracle_select rejected the arguments")
     return {"idx": idx, "n16": n16, "qbar": qbar, "kbar": kbar, "scores": scores}

@@ -247,6 +247,75 @@ static double block_score(const float *a, const float *b, int d) {
   return s;
 }
 
+/*
+ * Other block scores (the heuristic is the method's open risk: the
+ * hotpaper.ai summary of "ThriftAttention: Selective Mixed Precision for
+ * Long-Context FP4 Attention", section on significance and limits).  Each
+ * replaces the pooled-mean score; the budget rule, forced blocks and ranking
+ * stay the same.  All sums are fp64 and sequential in the order stated, so the
+ * GPU reproduces them bit for bit.
+ *   SCORE_MAX_POOLED   max over the 64 key rows r of block j of the dot
+ *                      product of the query block's pooled mean with k_r
+ *                      (channel order): one strong key is not averaged away.
+ *   SCORE_NORM_WEIGHTED  dot product of norm-weighted block means: row r of a
+ *                      block weighs w_r = its L2 norm (sqrt of the channel-order
+ *                      sum of squares); mean_c = (sum_r w_r x_rc) / (sum_r w_r),
+ *                      both sums in row order, rounded once to fp32 (0 for an
+ *                      all-zero block).
+ *   SCORE_BLOCK_MAX    max over every (query row, key row) pair of the two
+ *                      blocks of their exact dot product: the block's largest
+ *                      score, which needs all of Q K^T (a comparator, not a
+ *                      cheap heuristic).
+ */
+enum { SCORE_POOLED = 0, SCORE_MAX_POOLED = 1, SCORE_NORM_WEIGHTED = 2, SCORE_BLOCK_MAX = 3 };
+
+void oracle_normw_pool(const uint16_t *x16, int64_t BH, int N, int d, float *out) {
+  int nb = N / 64;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t bh = 0; bh < BH; bh++)
+    for (int i = 0; i < nb; i++) {
+      const uint16_t *blk = x16 + (bh * N + 64 * (int64_t)i) * d;
+      double w[64], wsum = 0.0;
+      for (int r = 0; r < 64; r++) {
+        double ss = 0.0;
+        for (int c = 0; c < d; c++) {
+          double x = half_bits_to_double(blk[r * d + c]);
+          ss = fma(x, x, ss);
+        }
+        w[r] = sqrt(ss);
+        wsum += w[r];
+      }
+      for (int c = 0; c < d; c++) {
+        double acc = 0.0;
+        for (int r = 0; r < 64; r++) acc = fma(w[r], half_bits_to_double(blk[r * d + c]), acc);
+        out[(bh * nb + i) * d + c] = wsum > 0.0 ? (float)(acc / wsum) : 0.0f;
+      }
+    }
+}
+
+/* max over the 64 key rows of block kblk of (query mean . k_r) */
+static double score_max_pooled(const float *q, const uint16_t *kblk, int d) {
+  double best = -INFINITY;
+  for (int r = 0; r < 64; r++) {
+    double s = 0.0;
+    for (int c = 0; c < d; c++) s += (double)q[c] * half_bits_to_double(kblk[r * d + c]);
+    if (s > best) best = s;
+  }
+  return best;
+}
+
+/* max over the 64 x 64 row pairs of (q_a . k_r) */
+static double score_block_max(const uint16_t *qblk, const uint16_t *kblk, int d) {
+  double best = -INFINITY;
+  for (int a = 0; a < 64; a++)
+    for (int r = 0; r < 64; r++) {
+      double s = 0.0;
+      for (int c = 0; c < d; c++) s += half_bits_to_double(qblk[a * d + c]) * half_bits_to_double(kblk[r * d + c]);
+      if (s > best) best = s;
+    }
+  return best;
+}
+
 int64_t oracle_list_entries(int B, int Hq, int N, int causal) {
   int64_t nb = N / 64;
   int64_t per = causal ? nb * (nb + 1) / 2 : nb * nb;
@@ -279,12 +348,19 @@ static int by_score_desc_then_index(const void *pa, const void *pb) {
  * n16[b,h,i] = FP16 list length.  scores (nullable) receives sigma(i,j) for
  * valid pairs in the same row layout.
  */
-int oracle_select(int B, int Hq, int Hkv, int N, int d, int causal, double frac, const uint16_t *q16,
-                  const uint16_t *k16, int32_t *idx, int32_t *n16, float *qbar, float *kbar, double *scores) {
+int oracle_select_kind(int kind, int B, int Hq, int Hkv, int N, int d, int causal, double frac,
+                       const uint16_t *q16, const uint16_t *k16, int32_t *idx, int32_t *n16, float *qbar,
+                       float *kbar, double *scores) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N % 64 || !(frac >= 0.0 && frac <= 1.0)) return ORC_EINVAL;
+  if (kind < SCORE_POOLED || kind > SCORE_BLOCK_MAX) return ORC_EINVAL;
   int nb = N / 64;
-  oracle_pool(q16, (int64_t)B * Hq, N, d, qbar);
-  oracle_pool(k16, (int64_t)B * Hkv, N, d, kbar);
+  if (kind == SCORE_NORM_WEIGHTED) {
+    oracle_normw_pool(q16, (int64_t)B * Hq, N, d, qbar);
+    oracle_normw_pool(k16, (int64_t)B * Hkv, N, d, kbar);
+  } else {
+    oracle_pool(q16, (int64_t)B * Hq, N, d, qbar);
+    oracle_pool(k16, (int64_t)B * Hkv, N, d, kbar);
+  }
   long long ppm = llround(frac * 1e6);
   int64_t per = causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
 #pragma omp parallel for collapse(3) schedule(dynamic, 4)
@@ -298,7 +374,14 @@ int oracle_select(int B, int Hq, int Hkv, int N, int d, int causal, double frac,
         scored_t *cand = malloc(sizeof(scored_t) * (size_t)nv);
         char *in16 = calloc((size_t)nv, 1);
         for (int j = 0; j < nv; j++) {
-          double s = block_score(qi, kbar + (((int64_t)b * Hkv + g) * nb + j) * d, d);
+          double s;
+          const uint16_t *kblk = k16 + (((int64_t)b * Hkv + g) * N + 64 * (int64_t)j) * d;
+          if (kind == SCORE_MAX_POOLED)
+            s = score_max_pooled(qi, kblk, d);
+          else if (kind == SCORE_BLOCK_MAX)
+            s = score_block_max(q16 + (((int64_t)b * Hq + h) * N + 64 * (int64_t)i) * d, kblk, d);
+          else
+            s = block_score(qi, kbar + (((int64_t)b * Hkv + g) * nb + j) * d, d);
           if (scores) scores[off + j] = s;
           cand[j].s = s;
           cand[j].j = j;
@@ -329,6 +412,12 @@ int oracle_select(int B, int Hq, int Hkv, int N, int d, int causal, double frac,
         free(in16);
       }
   return ORC_OK;
+}
+
+/* The library's default heuristic: pooled-mean scores. */
+int oracle_select(int B, int Hq, int Hkv, int N, int d, int causal, double frac, const uint16_t *q16,
+                  const uint16_t *k16, int32_t *idx, int32_t *n16, float *qbar, float *kbar, double *scores) {
+  return oracle_select_kind(SCORE_POOLED, B, Hq, Hkv, N, d, causal, frac, q16, k16, idx, n16, qbar, kbar, scores);
 }
 
 /* ------------------------------------------------------------------ */

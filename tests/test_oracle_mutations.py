@@ -33,6 +33,12 @@ MISTAKES = [
     ("ranking ascending", "if (a->s > b->s) return -1;", "if (a->s < b->s) return -1;"),
     ("weights reading: FP16 term unrounded", "if (rowsum == 1) l += p16;", "if (rowsum == 1) l += p[key];"),
     ("weights reading: FP4 group scale dropped", "l += e8m0_value(ps) * gw;", "l += gw;"),
+    ("max-pooled score misses the last key row",
+     "for (int r = 0; r < 64; r++) {\n    double s = 0.0;\n    for (int c = 0; c < d; c++) s += (double)q[c]",
+     "for (int r = 0; r < 63; r++) {\n    double s = 0.0;\n    for (int c = 0; c < d; c++) s += (double)q[c]"),
+    ("norm weights squared", "w[r] = sqrt(ss);", "w[r] = ss;"),
+    ("norm-weighted mean divided by the row count", "(float)(acc / wsum)", "(float)(acc / 64.0)"),
+    ("block max misses the last query row", "for (int a = 0; a < 64; a++)", "for (int a = 0; a < 63; a++)"),
 ]
 CONTROL = ("control: no change in meaning", "l += p[key];", "l += 1.0 * p[key];")
 

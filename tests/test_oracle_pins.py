@@ -477,3 +477,142 @@ def test_weights_rowsum_split_merge_equals_one_pass(orc, frac, tol):
         acc = sum(np.where(np.isfinite(s_["m"])[:, None], s_["acc"] * np.exp2(s_["m"] - M)[:, None], 0) for s_ in st)
         l = sum(np.where(np.isfinite(s_["m"]), s_["l"] * np.exp2(s_["m"] - M), 0) for s_ in st)
         assert np.abs(acc / l[:, None] - one["out"]).max() <= tol * np.abs(one["out"]).max()
+
+
+# ------------------------------------------------ heuristic variants (block scores)
+# The pages name the heuristic's robustness as the method's open risk (the
+# hotpaper.ai summary's section on significance and limits); the variants keep
+# the budget rule and change only the block score.
+
+
+def integer_blocks(seed, B, H, N, d, lo=-4, hi=4):
+    """fp16 bits of small integers: every block mean (a multiple of 1/64), every
+    product and every sum below stays exact in fp64, so numpy's order-free dot
+    products equal the oracle's sequential ones bit for bit."""
+    g = np.random.default_rng(seed)
+    x = g.integers(lo, hi + 1, size=(B, H, N, d)).astype(np.float16)
+    return x.view(np.uint16)
+
+
+def test_max_pooled_and_block_max_scores_equal_numpy_on_exact_inputs(orc):
+    B, Hq, Hkv, N, d = 1, 2, 1, 512, 32
+    q16, k16 = integer_blocks(21, B, Hq, N, d), integer_blocks(22, B, Hkv, N, d)
+    qv, kv = half_vals(q16), half_vals(k16)
+    nb = N // 64
+    qbar = qv.reshape(B, Hq, nb, 64, d).mean(axis=3)
+    kb = kv.reshape(B, Hkv, nb, 64, d)
+    qb = qv.reshape(B, Hq, nb, 64, d)
+    for score in ("max_pooled", "block_max"):
+        sel = orc.select(q16, k16, 0.3, True, score=score)
+        off = 0
+        for h in range(Hq):
+            for i in range(nb):
+                for j in range(i + 1):
+                    if score == "max_pooled":
+                        want = (kb[0, 0, j] @ qbar[0, h, i]).max()
+                    else:
+                        want = (qb[0, h, i] @ kb[0, 0, j].T).max()
+                    assert sel["scores"][off + j] == want, (score, h, i, j)
+                off += i + 1
+
+
+def test_variant_selection_brute_force_small(orc):
+    # nb = 8: for every variant the FP16 list is the forced blocks plus the
+    # best-total subset of the rest under that variant's scores (numpy)
+    B, Hq, Hkv, N, d = 1, 2, 1, 512, 32
+    q16, k16 = integer_blocks(31, B, Hq, N, d), integer_blocks(32, B, Hkv, N, d)
+    qv, kv = half_vals(q16), half_vals(k16)
+    qbar = qv.reshape(1, Hq, 8, 64, d).mean(axis=3)
+    kb, qb = kv.reshape(1, 1, 8, 64, d), qv.reshape(1, Hq, 8, 64, d)
+    for score in ("max_pooled", "block_max", "norm_weighted"):
+        for frac in (0.3, 0.6):
+            sel = orc.select(q16, k16, frac, True, score=score)
+            for h in range(Hq):
+                for i in range(8):
+                    if score == "max_pooled":
+                        sigma = np.array([(kb[0, 0, j] @ qbar[0, h, i]).max() for j in range(i + 1)])
+                    elif score == "block_max":
+                        sigma = np.array([(qb[0, h, i] @ kb[0, 0, j].T).max() for j in range(i + 1)])
+                    else:
+                        sigma = sel["qbar"][0, h, i].astype(np.float64) @ sel["kbar"][0, 0, : i + 1].astype(np.float64).T
+                    kk = expected_budget(frac, i + 1, i)
+                    forced = {0, i}
+                    rest = [j for j in range(i + 1) if j not in forced]
+                    best = max(itertools.combinations(rest, kk - len(forced)),
+                               key=lambda c: (sum(sigma[list(c)]), [-j for j in c]))
+                    l16, _ = orc.row_lists(sel, 1, Hq, N, True, 0, h, i)
+                    assert set(l16.tolist()) == forced | set(best), (score, frac, h, i)
+
+
+def test_max_pooled_finds_a_single_strong_key_that_the_mean_dilutes(orc):
+    # every query row is u; block 5 holds one key 8u among noise, block 3 is
+    # 0.3u in every row.  Pooled means rank block 3 first (0.3 > 8/64);
+    # max-pooling ranks block 5 first (8 > 0.3).  Budget at i = 7: 3 blocks.
+    d, N = 64, 512
+    g = np.random.default_rng(4)
+    u = g.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = np.tile(u, (1, 1, N, 1))
+    k = 0.01 * g.standard_normal((1, 1, N, d))
+    k[0, 0, 3 * 64: 4 * 64] = 0.3 * u
+    k[0, 0, 5 * 64 + 17] = 8.0 * u
+    q16, k16 = q.astype(np.float16).view(np.uint16), k.astype(np.float16).view(np.uint16)
+    pooled = orc.select(q16, k16, 0.3, True)
+    maxp = orc.select(q16, k16, 0.3, True, score="max_pooled")
+    l16_p, _ = orc.row_lists(pooled, 1, 1, N, True, 0, 0, 7)
+    l16_m, _ = orc.row_lists(maxp, 1, 1, N, True, 0, 0, 7)
+    assert l16_p.tolist() == [0, 3, 7]
+    assert l16_m.tolist() == [0, 5, 7]
+
+
+def test_norm_weighted_means_reduce_to_pooled_means_for_equal_norms(orc):
+    # every row holds one 3 and one 4 (norm exactly 5) in random channels:
+    # equal weights, so the weighted mean is the plain mean, bit for bit
+    g = np.random.default_rng(8)
+    B, H, N, d = 1, 2, 256, 64
+    x = np.zeros((B, H, N, d))
+    for h in range(H):
+        for t in range(N):
+            a, b = g.choice(d, 2, replace=False)
+            x[0, h, t, a] = 3.0 * g.choice([-1, 1])
+            x[0, h, t, b] = 4.0 * g.choice([-1, 1])
+    x16 = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.normw_pool(x16), orc.pool(x16))
+
+
+def test_norm_weighted_means_closed_form_and_numpy(orc):
+    # random rows: the weighted mean against numpy (fp64, other summation
+    # order) within an fp32 ulp; one row 100x the others dominates its block
+    g = np.random.default_rng(9)
+    B, H, N, d = 1, 1, 256, 64
+    x = g.standard_normal((B, H, N, d))
+    x[0, 0, 64 + 5] *= 100.0
+    x16 = x.astype(np.float16).view(np.uint16)
+    xv = half_vals(x16).reshape(B, H, N // 64, 64, d)
+    w = np.sqrt((xv ** 2).sum(-1, keepdims=True))
+    want = (w * xv).sum(-2) / w.sum(-2)
+    got = orc.normw_pool(x16).astype(np.float64)
+    np.testing.assert_allclose(got, want, rtol=2 ** -22, atol=1e-30)
+    # the dominant row: weight ~100 |x| against 63 rows of ~|x|
+    big = xv[0, 0, 1, 5]
+    assert np.linalg.norm(got[0, 0, 1] - big * w[0, 0, 1, 5, 0] / w[0, 0, 1].sum()) < 0.1 * np.linalg.norm(got[0, 0, 1])
+    # an all-zero block has mean 0
+    z = np.zeros((1, 1, 64, d), np.float16).view(np.uint16)
+    assert np.all(orc.normw_pool(z) == 0.0)
+
+
+def test_variant_lists_keep_the_selector_invariants(orc):
+    q, k, _ = synth.random_qkv(1, 4, 2, 1024, 64, "fp16", seed=17)
+    qz = orc.quantize(synth.bits(q), synth.bits(k), synth.bits(k), "fp16")
+    nb = 16
+    for score in ("max_pooled", "norm_weighted", "block_max"):
+        for frac in (0.0, 0.1, 1.0):
+            sel = orc.select(qz["q16"], qz["k16"], frac, True, score=score)
+            for h in range(4):
+                for i in range(nb):
+                    l16, l4 = orc.row_lists(sel, 1, 4, 1024, True, 0, h, i)
+                    assert np.all(np.diff(l16) > 0) and np.all(np.diff(l4) > 0)
+                    assert sorted(set(l16) | set(l4)) == list(range(i + 1))
+                    assert len(l16) == expected_budget(frac, i + 1, i)
+                    if frac > 0:
+                        assert 0 in l16 and i in l16
