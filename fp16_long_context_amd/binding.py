@@ -29,7 +29,7 @@ class Shape(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("thrift_quantize", "thrift_select_workspace_bytes", "thrift_list_entries", "thrift_select",
-           "thrift_select_noalloc",
+           "thrift_select_noalloc", "thrift_select_ex", "thrift_block_scores",
            "thrift_attn_fwd", "thrift_attn_fwd_wsum", "thrift_attn_fwd_ex", "thrift_attn_workspace_bytes",
            "thrift_status_str")
 
@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.thrift_select.restype = i32
         L.thrift_select_noalloc.argtypes = [SP, f64, P, P, P, P, P]
         L.thrift_select_noalloc.restype = i32
+        L.thrift_select_ex.argtypes = [SP, f64, i32, P, P, P, P, P, sz, P]
+        L.thrift_select_ex.restype = i32
+        L.thrift_block_scores.argtypes = [SP, i32, P, P, P, P, sz, P]
+        L.thrift_block_scores.restype = i32
         for fn in (L.thrift_attn_fwd, L.thrift_attn_fwd_wsum):
             fn.argtypes = [SP, f32] + [P] * 11 + [P, i32, P, P, sz, P]
             fn.restype = i32
@@ -151,10 +155,16 @@ def list_entries(B, Hq, N, causal=True) -> int:
     return int(lib().thrift_list_entries(ctypes.byref(s)))
 
 
+SCORES = {"pooled_mean": 0, "max_pooled": 1, "norm_weighted": 2, "block_max": 3}
+
+
 def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = True, workspace=None, idx=None,
-           n16=None):
+           n16=None, score: str = "pooled_mean"):
     """Traversal lists: idx (int32, per-row FP16 list then FP4 list) and n16 [B,Hq,nb].
-    idx, n16 and the workspace may be preallocated."""
+    idx, n16 and the workspace may be preallocated.  score: the block score
+    ("pooled_mean" = thrift_select; the others go through thrift_select_ex)."""
+    if score not in SCORES:
+        raise ThriftError(f"score must be one of {sorted(SCORES)}")
     if q16.dim() != 4 or k16.dim() != 4 or q16.dtype != torch.float16 or k16.dtype != torch.float16:
         raise ThriftError("q16 and k16 must be 4-D fp16 tensors")
     B, Hq, N, d = q16.shape
@@ -176,10 +186,41 @@ def select(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = Tru
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q16.device)
     _need_gpu(q16, k16, idx, n16, workspace)
-    rc = L.thrift_select(ctypes.byref(s), float(frac), _ptr(q16), _ptr(k16), _ptr(idx), _ptr(n16), _ptr(workspace),
-                         workspace.numel() * workspace.element_size(), _stream(q16.device))
+    wsn = workspace.numel() * workspace.element_size()
+    if score == "pooled_mean":
+        rc = L.thrift_select(ctypes.byref(s), float(frac), _ptr(q16), _ptr(k16), _ptr(idx), _ptr(n16),
+                             _ptr(workspace), wsn, _stream(q16.device))
+    else:
+        rc = L.thrift_select_ex(ctypes.byref(s), float(frac), SCORES[score], _ptr(q16), _ptr(k16), _ptr(idx),
+                                _ptr(n16), _ptr(workspace), wsn, _stream(q16.device))
     _check(rc, "thrift_select")
     return idx, n16
+
+
+def block_scores(q16: torch.Tensor, k16: torch.Tensor, score: str = "pooled_mean", causal: bool = True):
+    """thrift_block_scores: the fp32 block scores sigma(i, j) the selection ranks,
+    in the list layout (flat, thrift_list_entries entries)."""
+    if score not in SCORES:
+        raise ThriftError(f"score must be one of {sorted(SCORES)}")
+    if q16.dim() != 4 or k16.dim() != 4 or q16.dtype != torch.float16 or k16.dtype != torch.float16:
+        raise ThriftError("q16 and k16 must be 4-D fp16 tensors")
+    B, Hq, N, d = q16.shape
+    Hkv = k16.shape[1]
+    if tuple(k16.shape) != (B, Hkv, N, d):
+        raise ThriftError(f"k16 must be [B,Hkv,N,d] = [{B},Hkv,{N},{d}]; got {tuple(k16.shape)}")
+    s = make_shape(B, Hq, Hkv, N, d, causal)
+    L = lib()
+    ents = int(L.thrift_list_entries(ctypes.byref(s)))
+    wsb = int(L.thrift_select_workspace_bytes(ctypes.byref(s)))
+    if ents <= 0 or wsb <= 0:
+        raise ThriftError("unsupported shape")
+    out = torch.empty(ents, dtype=torch.float32, device=q16.device)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=q16.device)
+    _need_gpu(q16, k16, out, ws)
+    rc = L.thrift_block_scores(ctypes.byref(s), SCORES[score], _ptr(q16), _ptr(k16), _ptr(out), _ptr(ws), wsb,
+                               _stream(q16.device))
+    _check(rc, "thrift_block_scores")
+    return out
 
 
 def select_noalloc(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bool = True, idx=None, n16=None):

@@ -18,9 +18,10 @@ int check_shape(const thrift_shape *s) {
   if (s->d != 64 && s->d != 128) return THRIFT_EUNSUPPORTED;
   if (s->block != 64) return THRIFT_EUNSUPPORTED;
   if (s->N % 64 != 0 || s->N / 64 > kMaxBlocks) return THRIFT_EUNSUPPORTED;
-  // grid sizes fit 32 bits
+  // one workgroup of up to 256 threads per (b, query head, query block): a
+  // launch addresses fewer than 2^32 threads, so B * Hq * N/64 < 2^24
   const int64_t rows = (int64_t)s->B * s->Hq * (s->N / 64);
-  if (rows > 0x7fffffffLL) return THRIFT_EUNSUPPORTED;
+  if (rows >= (1LL << 24)) return THRIFT_EUNSUPPORTED;
   return THRIFT_OK;
 }
 
@@ -90,6 +91,45 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
   a.ppm = (int64_t)llround(frac * 1e6);
   return launch_select(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
+static int select_args(const thrift_shape *s, double frac, int score, const void *q16, const void *k16,
+                       int32_t *idx, int32_t *n16, void *workspace, size_t ws_bytes, SelectArgs &a) {
+  int rc = check_shape(s);
+  if (rc != THRIFT_OK) return rc;
+  if (!(frac >= 0.0 && frac <= 1.0)) return THRIFT_EINVAL;  // also rejects NaN
+  if (score < THRIFT_SCORE_POOLED_MEAN || score > THRIFT_SCORE_BLOCK_MAX) return THRIFT_EINVAL;
+  const void *ptrs[] = {q16, k16, idx, n16};
+  for (const void *p : ptrs)
+    if (!aligned_ok(p)) return THRIFT_EINVAL;
+  const size_t need = thrift_select_workspace_bytes(s);
+  if (!workspace || ws_bytes < need) return THRIFT_EWORKSPACE;
+  if (!aligned_ok(workspace)) return THRIFT_EINVAL;
+  a.q16 = (const uint16_t *)q16; a.k16 = (const uint16_t *)k16;
+  a.idx = idx; a.n16 = n16;
+  a.qbar = (float *)workspace;
+  a.kbarT = (float *)workspace + (size_t)s->B * s->Hq * (s->N / 64) * s->d;
+  a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
+  a.ppm = (int64_t)llround(frac * 1e6);
+  a.kind = score;
+  return THRIFT_OK;
+}
+
+int thrift_select_ex(const thrift_shape *s, double frac, int score, const void *q16, const void *k16, int32_t *idx,
+                     int32_t *n16, void *workspace, size_t ws_bytes, void *stream) {
+  SelectArgs a;
+  const int rc = select_args(s, frac, score, q16, k16, idx, n16, workspace, ws_bytes, a);
+  if (rc != THRIFT_OK) return rc;
+  return launch_select(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
+int thrift_block_scores(const thrift_shape *s, int score, const void *q16, const void *k16, float *scores,
+                        void *workspace, size_t ws_bytes, void *stream) {
+  SelectArgs a;
+  // n16 is not written: any aligned non-null pointer passes validation
+  const int rc = select_args(s, 1.0, score, q16, k16, (int32_t *)scores, (int32_t *)scores, workspace, ws_bytes, a);
+  if (rc != THRIFT_OK) return rc;
+  return launch_block_scores(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
 }
 
 int thrift_select_noalloc(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx,

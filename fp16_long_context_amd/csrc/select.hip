@@ -166,6 +166,217 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectArgs a, int 
 }
 
 // ---------------------------------------------------------------------------
+// Other block scores (the heuristic is the method's open risk: the
+// hotpaper.ai summary of the ThriftAttention paper, section on significance
+// and limits).  Each replaces the pooled mean; the selection is unchanged.
+// All chains are fp64 in the order stated, as in the pooled score.
+enum { kScorePooled = 0, kScoreMaxPooled = 1, kScoreNormWeighted = 2, kScoreBlockMax = 3 };
+
+__device__ __forceinline__ double half_to_double(const uint16_t h) { return (double)__builtin_bit_cast(_Float16, h); }
+
+// Norm-weighted mean of one 64-row block per workgroup: row r weighs its L2
+// norm w_r (sqrt of the fma chain of squares over the channels in order);
+// mean_c = (fma chain of w_r x_rc over the rows in order) / (sum of w_r in
+// row order), rounded once to fp32, 0 for an all-zero block.  Q means go
+// row-major [BH, nb, d], K means channel-major [BH, d, nb], as pool_kernel.
+template <bool TRANSPOSED>
+__global__ __launch_bounds__(128) void normw_pool_kernel(const uint16_t *__restrict__ x16, float *__restrict__ out,
+                                                         int N, int d) {
+  __shared__ double w[64];
+  __shared__ double wsum;
+  const int nb = N / 64;
+  const int64_t bi = blockIdx.x;  // = bh * nb + i
+  const int64_t bh = bi / nb;
+  const int i = (int)(bi % nb);
+  const uint16_t *blk = x16 + (bh * N + 64 * (int64_t)i) * d;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    double ss = 0.0;
+    for (int c = 0; c < d; c++) {
+      const double x = half_to_double(blk[(int64_t)tid * d + c]);
+      ss = fma(x, x, ss);
+    }
+    w[tid] = sqrt(ss);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double s = 0.0;
+    for (int r = 0; r < 64; r++) s += w[r];
+    wsum = s;
+  }
+  __syncthreads();
+  for (int c = tid; c < d; c += 128) {
+    double acc = 0.0;
+    for (int r = 0; r < 64; r++) acc = fma(w[r], half_to_double(blk[(int64_t)r * d + c]), acc);
+    const float m = wsum > 0.0 ? (float)(acc / wsum) : 0.0f;
+    if (TRANSPOSED)
+      out[(bh * d + c) * nb + i] = m;
+    else
+      out[bi * d + c] = m;
+  }
+}
+
+// Tile (ti, tj) of head-tile index t (as score_kernel).
+__device__ __forceinline__ void tile_of(const int t, const int causal, const int tn, int &ti, int &tj) {
+  if (causal) {
+    ti = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ti++;
+    while (ti * (ti + 1) / 2 > t) ti--;
+    tj = t - ti * (ti + 1) / 2;
+  } else {
+    ti = t / tn;
+    tj = t % tn;
+  }
+}
+
+// Max-pooled scores: the 64 x 64 block-pair tile of score_kernel, with the
+// key side one row r of every key block at a time: the query means stay in
+// LDS (fp64, channel-major) while the 64 key rows r of the tile's blocks are
+// staged for each r; thread t keeps the running max of its 16 chains.
+template <int D>
+__global__ __launch_bounds__(kScoreThreads) void maxpool_score_kernel(SelectArgs a, int tiles_per_head, int tn) {
+  extern __shared__ __attribute__((aligned(16))) double sm[];
+  double *qs = sm, *ks = sm + D * kQStride;
+  const int nb = a.N / 64;
+  const int64_t bh = blockIdx.x / tiles_per_head;
+  int ti, tj;
+  tile_of(blockIdx.x % tiles_per_head, a.causal, tn, ti, tj);
+  const int i0 = 64 * ti, j0 = 64 * tj;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int g = (int)((int64_t)h * a.Hkv / a.Hq);
+  const int tid = threadIdx.x;
+  const float *qb = a.qbar + (bh * nb + i0) * (int64_t)D;
+  for (int e = tid; e < 64 * D; e += kScoreThreads) {
+    const int r = e / D, c = e % D;
+    qs[c * kQStride + r] = (i0 + r < nb) ? (double)qb[(int64_t)min(r, nb - 1 - i0) * D + c] : 0.0;
+  }
+  const uint16_t *kh = a.k16 + ((int64_t)b * a.Hkv + g) * a.N * (int64_t)D;
+  const int qi = 4 * (tid >> 4), kj = 4 * (tid & 15);
+  double best[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) best[u][v] = -INFINITY;
+  for (int r = 0; r < 64; r++) {
+    __syncthreads();  // the previous row's reads are done (and the Q tile is staged)
+    for (int e = tid; e < 64 * D; e += kScoreThreads) {
+      const int jj = e / D, c = e % D;
+      const int j = min(j0 + jj, nb - 1);  // in bounds; blocks past nb are never written
+      ks[c * 64 + jj] = half_to_double(kh[((int64_t)64 * j + r) * D + c]);
+    }
+    __syncthreads();
+    double s[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) s[u][v] = 0.0;
+#pragma unroll 4
+    for (int c = 0; c < D; c++) {
+      const double2 q01 = *(const double2 *)(qs + c * kQStride + qi);
+      const double2 q23 = *(const double2 *)(qs + c * kQStride + qi + 2);
+      const double2 k01 = *(const double2 *)(ks + c * 64 + kj);
+      const double2 k23 = *(const double2 *)(ks + c * 64 + kj + 2);
+      const double qd[4] = {q01.x, q01.y, q23.x, q23.y}, kd[4] = {k01.x, k01.y, k23.x, k23.y};
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) s[u][v] = fma(qd[u], kd[v], s[u][v]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) best[u][v] = fmax(best[u][v], s[u][v]);
+  }
+  const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
+  int32_t *base = a.idx + bh * per;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int i = i0 + qi + u;
+    if (i >= nb) continue;
+    const int nv = a.causal ? i + 1 : nb;
+    int32_t *row = base + row_offset(i, nb, a.causal);
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int j = j0 + kj + v;
+      if (j < nv) row[j] = __float_as_int((float)best[u][v]);
+    }
+  }
+}
+
+// Block-max scores: a workgroup per valid (b, h_q, i, j) at a time (grid
+// stride: B Hq times the valid pairs can exceed what one launch addresses):
+// both blocks' 64 rows staged in LDS (fp64, channel-major), thread t runs 16
+// of the 4096 row-pair chains, and the workgroup takes the max.
+template <int D>
+__device__ void blockmax_pair(const SelectArgs &a, const int64_t per, const int64_t bh, const int64_t p) {
+  extern __shared__ __attribute__((aligned(16))) double sm[];
+  __shared__ double wmax[kScoreThreads / 64];
+  double *qs = sm, *ks = sm + D * kQStride;
+  const int nb = a.N / 64;
+  int i, j;
+  if (a.causal) {
+    i = (int)((sqrt(8.0 * (double)p + 1.0) - 1.0) * 0.5);
+    while ((int64_t)(i + 1) * (i + 2) / 2 <= p) i++;
+    while ((int64_t)i * (i + 1) / 2 > p) i--;
+    j = (int)(p - (int64_t)i * (i + 1) / 2);
+  } else {
+    i = (int)(p / nb);
+    j = (int)(p % nb);
+  }
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int g = (int)((int64_t)h * a.Hkv / a.Hq);
+  const uint16_t *qblk = a.q16 + (bh * a.N + 64 * (int64_t)i) * D;
+  const uint16_t *kblk = a.k16 + (((int64_t)b * a.Hkv + g) * a.N + 64 * (int64_t)j) * D;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 64 * D; e += kScoreThreads) {
+    const int r = e / D, c = e % D;
+    qs[c * kQStride + r] = half_to_double(qblk[e]);
+    ks[c * 64 + r] = half_to_double(kblk[e]);
+  }
+  __syncthreads();
+  const int qi = 4 * (tid >> 4), kj = 4 * (tid & 15);
+  double s[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) s[u][v] = 0.0;
+#pragma unroll 4
+  for (int c = 0; c < D; c++) {
+    const double2 q01 = *(const double2 *)(qs + c * kQStride + qi);
+    const double2 q23 = *(const double2 *)(qs + c * kQStride + qi + 2);
+    const double2 k01 = *(const double2 *)(ks + c * 64 + kj);
+    const double2 k23 = *(const double2 *)(ks + c * 64 + kj + 2);
+    const double qd[4] = {q01.x, q01.y, q23.x, q23.y}, kd[4] = {k01.x, k01.y, k23.x, k23.y};
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) s[u][v] = fma(qd[u], kd[v], s[u][v]);
+  }
+  double m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) m = fmax(m, s[u][v]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    double best = wmax[0];
+    for (int w = 1; w < kScoreThreads / 64; w++) best = fmax(best, wmax[w]);
+    const int64_t tri = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
+    a.idx[bh * tri + row_offset(i, nb, a.causal) + j] = __float_as_int((float)best);
+  }
+  __syncthreads();  // the next pair restages qs/ks and wmax
+}
+
+template <int D>
+__global__ __launch_bounds__(kScoreThreads) void blockmax_score_kernel(SelectArgs a, int64_t per) {
+  const int64_t total = (int64_t)a.B * a.Hq * per;
+  for (int64_t w = blockIdx.x; w < total; w += gridDim.x) blockmax_pair<D>(a, per, w / per, w % per);
+}
+
+// ---------------------------------------------------------------------------
 // Selection: one wave per (b, h_q, query block i).
 constexpr int kSelThreads = 256;
 
@@ -243,6 +454,30 @@ __device__ __forceinline__ double exact_score(const float *qrow, const float *kT
   return s;
 }
 
+// The fp64 block score of kind `kind` for key block j of a query row: the
+// pooled or norm-weighted means' chain (qrow, kT), the max over the key rows
+// of (qrow . k_r), or the max over every row pair of the two blocks.
+template <int D>
+__device__ double exact_score_kind(const int kind, const float *qrow, const float *kT, const int nb,
+                                   const uint16_t *qblk, const uint16_t *kh, const int j) {
+  if (kind == kScoreMaxPooled || kind == kScoreBlockMax) {
+    const uint16_t *kblk = kh + (int64_t)64 * j * D;
+    double best = -INFINITY;
+    const int na = kind == kScoreBlockMax ? 64 : 1;
+    for (int q = 0; q < na; q++)
+      for (int r = 0; r < 64; r++) {
+        double s = 0.0;
+        for (int c = 0; c < D; c++) {
+          const double qv = kind == kScoreBlockMax ? half_to_double(qblk[q * D + c]) : (double)qrow[c];
+          s = fma(qv, half_to_double(kblk[r * D + c]), s);
+        }
+        best = fmax(best, s);
+      }
+    return best;
+  }
+  return exact_score<D>(qrow, kT, nb, j);
+}
+
 // KPL: keys per lane, at least ceil(nb / 64).  Lane l holds blocks l + 64 t.
 // LDS: nb 64-bit keys per wave for the blocks tied at the fp32 cut-off.
 template <int D, int KPL>
@@ -309,12 +544,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a, int w
       const int g = (int)((int64_t)(bh % a.Hq) * a.Hkv / a.Hq), b = (int)(bh / a.Hq);
       const float *qrow = a.qbar + row * (int64_t)D;
       const float *kT = a.kbarT + ((int64_t)b * a.Hkv + g) * D * (int64_t)nb;
+      const uint16_t *kh = a.k16 + ((int64_t)b * a.Hkv + g) * a.N * (int64_t)D;
+      const uint16_t *qblk = a.q16 + (bh * a.N + 64 * (int64_t)i) * D;
       uint64_t mx = 0, mn = ~0ull;
 #pragma unroll
       for (int t = 0; t < KPL; t++) {
         const int j = lane + 64 * t;
         uint64_t k64 = 0;
-        if (key[t] == T) k64 = order_key64(exact_score<D>(qrow, kT, nb, j));
+        if (key[t] == T) k64 = order_key64(exact_score_kind<D>(a.kind, qrow, kT, nb, qblk, kh, j));
         if (j < nb) tk[j] = k64;
         mx = k64 > mx ? k64 : mx;
         mn = (k64 && k64 < mn) ? k64 : mn;
@@ -410,19 +647,58 @@ static hipError_t launch_select_kpl(const SelectArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The block scores of a.kind into a.idx (fp32 bits at the list positions);
+// the means they need go to a.qbar / a.kbarT first.
+template <int D>
+static hipError_t launch_scores_d(const SelectArgs &a, hipStream_t st) {
+  const int nb = a.N / 64;
+  auto grid = [](int64_t work) {
+    int64_t b = (work + 255) / 256;
+    return (unsigned)(b > 256 * 64 ? 256 * 64 : b);
+  };
+  const int64_t BHq = (int64_t)a.B * a.Hq, BHk = (int64_t)a.B * a.Hkv;
+  hipError_t e;
+  if (a.kind == kScoreNormWeighted) {
+    hipLaunchKernelGGL(normw_pool_kernel<false>, dim3((unsigned)(BHq * nb)), dim3(128), 0, st, a.q16, a.qbar, a.N, D);
+    hipLaunchKernelGGL(normw_pool_kernel<true>, dim3((unsigned)(BHk * nb)), dim3(128), 0, st, a.k16, a.kbarT, a.N, D);
+  } else if (a.kind != kScoreBlockMax) {
+    hipLaunchKernelGGL(pool_kernel<false>, dim3(grid(BHq * nb * D)), dim3(256), 0, st, a.q16, a.qbar, BHq, a.N, D);
+    if (a.kind == kScorePooled)
+      hipLaunchKernelGGL(pool_kernel<true>, dim3(grid(BHk * nb * D)), dim3(256), 0, st, a.k16, a.kbarT, BHk, a.N, D);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int tn = (nb + 63) / 64;
+  const int tiles = a.causal ? tn * (tn + 1) / 2 : tn * tn;
+  if (a.kind == kScorePooled || a.kind == kScoreNormWeighted) {
+    if ((e = hipFuncSetAttribute((const void *)score_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 kScoreLds)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(score_kernel<D>, dim3((unsigned)(BHq * tiles)), dim3(kScoreThreads), kScoreLds, st, a, tiles,
+                       tn);
+  } else {
+    const int lds = D * (kQStride + 64) * 8;
+    const void *fn = a.kind == kScoreMaxPooled ? (const void *)maxpool_score_kernel<D>
+                                               : (const void *)blockmax_score_kernel<D>;
+    if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
+    if (a.kind == kScoreMaxPooled) {
+      hipLaunchKernelGGL(maxpool_score_kernel<D>, dim3((unsigned)(BHq * tiles)), dim3(kScoreThreads), lds, st, a,
+                         tiles, tn);
+    } else {
+      const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
+      const int64_t work = BHq * per;
+      const unsigned g = (unsigned)(work < 65536 * 16 ? work : 65536 * 16);  // grid stride beyond 1M workgroups
+      hipLaunchKernelGGL(blockmax_score_kernel<D>, dim3(g), dim3(kScoreThreads), lds, st, a, per);
+    }
+  }
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_select_d(const SelectArgs &a, hipStream_t st) {
   const int nb = a.N / 64;
   if (a.ppm > 0) {
-    const int tn = (nb + 63) / 64;
-    const int tiles = a.causal ? tn * (tn + 1) / 2 : tn * tn;
-    const size_t lds = kScoreLds;
-    hipError_t e = hipFuncSetAttribute((const void *)score_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    const hipError_t e = launch_scores_d<D>(a, st);
     if (e != hipSuccess) return e;
-    const int64_t grid = (int64_t)a.B * a.Hq * tiles;
-    hipLaunchKernelGGL(score_kernel<D>, dim3((unsigned)grid), dim3(kScoreThreads), lds, st, a, tiles, tn);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int kpl = (nb + 63) / 64;
   if (kpl <= 1) return launch_select_kpl<D, 1>(a, st);
@@ -436,19 +712,11 @@ static hipError_t launch_select_d(const SelectArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t st) {
-  const int nb = a.N / 64;
-  auto grid = [](int64_t work) {
-    int64_t b = (work + 255) / 256;
-    return (unsigned)(b > 256 * 64 ? 256 * 64 : b);
-  };
-  const int64_t BHq = (int64_t)a.B * a.Hq, BHk = (int64_t)a.B * a.Hkv;
-  if (a.ppm > 0) {
-    hipLaunchKernelGGL(pool_kernel<false>, dim3(grid(BHq * nb * a.d)), dim3(256), 0, st, a.q16, a.qbar, BHq, a.N,
-                       a.d);
-    hipLaunchKernelGGL(pool_kernel<true>, dim3(grid(BHk * nb * a.d)), dim3(256), 0, st, a.k16, a.kbarT, BHk, a.N,
-                       a.d);
-  }
   return a.d == 64 ? launch_select_d<64>(a, st) : launch_select_d<128>(a, st);
+}
+
+hipError_t launch_block_scores(const SelectArgs &a, hipStream_t st) {
+  return a.d == 64 ? launch_scores_d<64>(a, st) : launch_scores_d<128>(a, st);
 }
 
 // ---------------------------------------------------------------------------

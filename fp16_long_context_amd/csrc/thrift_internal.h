@@ -52,6 +52,7 @@ struct SelectArgs {
   float *kbarT;  // [B,Hkv,d,nb]
   int B, Hq, Hkv, N, d, causal;
   int64_t ppm;
+  int kind = 0;  // block score: 0 pooled mean, 1 max-pooled, 2 norm-weighted, 3 block max
 };
 
 struct AttnArgs {
@@ -72,6 +73,9 @@ struct AttnArgs {
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t st);
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
+// The block scores of a.kind alone, rounded to fp32, written (as bits) into
+// a.idx at the list positions (no selection).
+hipError_t launch_block_scores(const SelectArgs &a, hipStream_t st);
 // Bytes of the static device array that holds the pooled means for
 // launch_select_scratch (which ignores a.qbar / a.kbarT and points them into
 // that array); callers check 4 * nb * d * B * (Hq + Hkv) against it first.

@@ -12,9 +12,10 @@ benchmarks with trained models; here the planted-needle workloads stand in:
 * length_sweep(): the same at several sequence lengths of one generator;
 * attribution(): the gain of computing single blocks in FP16, against the
   selection heuristic's block score and the exact attention mass;
-* heuristics(): the output error when the FP16 blocks are picked by other
-  block scores (max-pooled, norm-weighted, exact block max) or at a block
-  size of 128, under the same budget rule, through caller-built lists.
+* heuristics(): the output error when the FP16 blocks are picked by the
+  other block scores the library offers (thrift_select_ex: max-pooled,
+  norm-weighted, exact block max) under the same budget rule, and what each
+  selection costs.
 
 Everything runs through the library (quantize, select, attention); nothing
 here is an oracle.
@@ -178,15 +179,12 @@ def attribution(workload: str = "llama8b_16k", N: int | None = None, frac: float
         binding.attn_fwd(qz, idx, n16, True, out=buf, workspace=ws)
         rows = ar[delta:]
         gain[:, :, rows, rows - delta] = (base - block_err(buf))[:, :, rows]
-    # heuristic score: dot product of pooled block means (fp32 means, fp64 dot)
-    qbar = qz["q16"].float().view(B, Hq, nb, 64, d).mean(3).double()
-    kbar = qz["k16"].float().view(B, Hkv, nb, 64, d).mean(3).double()
-    kb = kbar.repeat_interleave(grp, dim=1)  # [B,Hq,nb,d]
-    score = torch.matmul(qbar, kb.transpose(-1, -2).contiguous())
-    # exact attention mass of each block under FP16 attention, and the
-    # block's largest exact score (a block-max heuristic to compare with)
+    # the heuristic's block score and the block's largest exact score, as the
+    # library computes them (thrift_block_scores), on a [B,Hq,nb,nb] grid
+    score = scores_grid(binding.block_scores(qz["q16"], qz["k16"], "pooled_mean"), B, Hq, nb)
+    bmax = scores_grid(binding.block_scores(qz["q16"], qz["k16"], "block_max"), B, Hq, nb)
+    # exact attention mass of each block under FP16 attention
     mass = torch.zeros((B, Hq, nb, nb), dtype=torch.float64, device=dev)
-    bmax = torch.full((B, Hq, nb, nb), float("-inf"), dtype=torch.float64, device=dev)
     sm = 1.0 / math.sqrt(d)
     kf = qz["k16"].float()
     for b in range(B):
@@ -203,8 +201,6 @@ def attribution(workload: str = "llama8b_16k", N: int | None = None, frac: float
                     p_ = torch.nn.functional.pad(p_, (0, pad))
                 m_ = p_.view((r1 - r0) // 64, 64, -1, 64).sum((1, 3), dtype=torch.float64)
                 mass[b, h, r0 // 64:r1 // 64, : m_.shape[1]] = m_
-                x_ = s_.view((r1 - r0) // 64, 64, -1, 64).amax(dim=(1, 3)).double()
-                bmax[b, h, r0 // 64:r1 // 64, : x_.shape[1]] = x_
     valid = ~torch.isnan(gain)
     g_all, s_all, m_all = gain[valid], score[valid], mass[valid]
     res = {
@@ -245,95 +241,34 @@ def attribution(workload: str = "llama8b_16k", N: int | None = None, frac: float
     return res
 
 
-def pooled_means(x16, rows: int = 64):
-    """fp32 means of `rows`-row blocks of [..., N, d] fp16: the exact fp64 sum
-    of the block, scaled and rounded to fp32 once (the selector's pooling)."""
-    N, d = x16.shape[-2], x16.shape[-1]
-    xd = x16.double().reshape(*x16.shape[:-2], N // rows, rows, d)
-    return (xd.sum(-2) * (1.0 / rows)).float()
-
-
-def sequential_scores(qbar, kbar):
-    """fp64 dot products of [..., nq, d] and [..., nk, d] fp32 means, summed
-    in channel order (each product of two fp32 values is exact in fp64, so
-    this matches an fma chain in that order bit for bit): [..., nq, nk]."""
+def scores_grid(flat, B: int, Hq: int, nb: int):
+    """Causal block scores in the list layout (row i of each head at
+    i(i+1)/2, entry j) -> a [B,Hq,nb,nb] fp64 grid, -inf above the diagonal."""
     import torch
 
-    qd, kd = qbar.double(), kbar.double()
-    s = torch.zeros(qd.shape[:-1] + (kd.shape[-2],), dtype=torch.float64, device=qd.device)
-    for c in range(qd.shape[-1]):
-        s = s + qd[..., :, c, None] * kd[..., None, :, c]
-    return s
-
-
-def select_mask(score, frac: float, causal: bool = True):
-    """FP16 blocks of every row block under the selector's budget rule, for
-    any block score [..., nb, nb]: with ppm = round(frac * 1e6), no FP16 blocks
-    at ppm = 0; else the first and diagonal blocks are forced and the
-    best-scoring others are added up to k = min(n_valid, max(|forced|,
-    ceil(ppm * n_valid / 1e6))) blocks in all, ties to the lower block index.
-    Returns a bool mask [..., nb, nb]."""
-    import torch
-
-    nb = score.shape[-1]
-    dev = score.device
+    dev = flat.device
     ar = torch.arange(nb, device=dev)
-    i, j = ar[:, None], ar[None, :]
-    valid = (j <= i) if causal else torch.ones(nb, nb, dtype=torch.bool, device=dev)
-    ppm = int(math.floor(frac * 1e6 + 0.5))  # llround for frac >= 0
-    if ppm == 0:
-        return torch.zeros(score.shape, dtype=torch.bool, device=dev)
-    nv = valid.sum(-1)
-    forced = (j == 0) | (j == i)
-    nforced = forced.sum(-1)
-    k = torch.minimum(nv, torch.maximum(nforced, (ppm * nv + 999999) // 1000000))
-    key = score.double().masked_fill(~valid, float("-inf")).masked_fill(forced, float("inf"))
-    order = torch.sort(key, dim=-1, descending=True, stable=True).indices
-    rank = torch.empty_like(order)
-    rank.scatter_(-1, order, ar.expand_as(order).contiguous())
-    return (rank < k[:, None]) & valid
-
-
-def lists_from_mask(fp16, causal: bool = True):
-    """(idx, n16) in the library's list layout from a bool FP16 mask
-    [B, Hq, nb, nb]: per row block the FP16 blocks ascending, then the other
-    valid blocks ascending."""
-    import torch
-
-    B, Hq, nb, _ = fp16.shape
-    dev = fp16.device
-    ar = torch.arange(nb, device=dev)
-    valid = (ar[None, :] <= ar[:, None]) if causal else torch.ones(nb, nb, dtype=torch.bool, device=dev)
-    fp16 = fp16 & valid
-    skey = torch.where(valid, (~fp16).long() * nb + ar, 2 * nb + ar)
-    order = torch.argsort(skey, dim=-1)
-    idx = order[:, :, valid.sum(-1)[:, None] > ar[None, :]].to(torch.int32).reshape(-1).contiguous()
-    return idx, fp16.sum(-1).to(torch.int32).contiguous()
-
-
-def expand_mask(fp16_big, factor: int):
-    """An FP16 mask over blocks of factor*64 rows expanded to 64-row blocks
-    (causally clipped by the list builder)."""
-    return fp16_big.repeat_interleave(factor, dim=-2).repeat_interleave(factor, dim=-1)
+    rb = torch.repeat_interleave(ar, ar + 1)
+    pos = torch.arange(nb * (nb + 1) // 2, device=dev) - rb * (rb + 1) // 2
+    g = torch.full((B, Hq, nb * nb), float("-inf"), dtype=torch.float64, device=dev)
+    g[:, :, rb * nb + pos] = flat.view(B, Hq, -1).double()
+    return g.view(B, Hq, nb, nb)
 
 
 def heuristics(workload: str = "long_128k", N: int | None = None, frac: float = 0.05, log=None) -> list:
-    """Output error of the mixed path when the FP16 blocks come from other
-    block scores, each under the selector's budget rule (first and diagonal
-    blocks forced), run through the library with caller-built lists:
+    """Output error of the mixed path when the FP16 blocks come from the
+    library's other block scores (thrift_select_ex), each under the same
+    budget rule (first and diagonal blocks forced):
 
-    * pooled_mean: the selector's own score (q-block mean . k-block mean); its
-      lists are checked to equal the library's selection;
+    * pooled_mean: the selector's own score (thrift_select);
     * max_pooled: max over the key rows r of block j of (q-block mean . k_r),
       so a single strong key is not averaged away;
     * norm_weighted: block means weighted by each row's L2 norm;
     * block_max: the block's largest exact score (needs the full QK^T; a
-      comparator, not a cheap heuristic);
-    * pooled_mean_128: the selector's score and rule on 128-row blocks, each
-      selected 128-block pair expanded to its four 64-row tile pairs.
+      comparator, not a cheap heuristic).
 
-    Each entry: err and needle-row err against the all-FP16 output, and the
-    share of causal tiles computed in FP16.
+    Each entry: err and needle-row err against the all-FP16 output, the
+    share of causal tiles computed in FP16, and the selection's time.
     """
     import torch
 
@@ -345,7 +280,6 @@ def heuristics(workload: str = "long_128k", N: int | None = None, frac: float = 
     w = x["w"]
     B, Hq, Hkv, Nn, d = w.B, w.Hq, w.Hkv, w.N, w.d
     nb = Nn // 64
-    grp = Hq // Hkv
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     qz = binding.quantize(q, k, v)
     del q, k, v
@@ -358,57 +292,32 @@ def heuristics(workload: str = "long_128k", N: int | None = None, frac: float = 
     tiles = B * Hq * nb * (nb + 1) // 2
     out = []
 
-    def run(name, idx, n16):
+    def run(name, idx, n16, **extra):
         o, _ = binding.attn_fwd(qz, idx, n16, True, workspace=ws)
         r = {"heuristic": name, "workload": workload, "N": Nn, "frac": frac,
              "err": round(torch.linalg.vector_norm(o - ref).item() / ref_norm, 6),
              "needle_err": round(torch.linalg.vector_norm(o.reshape(-1, d)[rows] - r2).item() / r2_norm, 6),
-             "fp16_tile_share": round(float(n16.sum()) / tiles, 5)}
+             "fp16_tile_share": round(float(n16.sum()) / tiles, 5), **extra}
         if log:
             log(json.dumps(r))
         out.append(r)
 
-    lib_idx, lib_n16 = binding.select(qz["q16"], qz["k16"], frac, True)
-    run("library_select", lib_idx, lib_n16)
     idx0, n160 = binding.select(qz["q16"], qz["k16"], 0.0, True)
     run("fp4_only", idx0, n160)
     del idx0, n160
-
-    q16, k16 = qz["q16"], qz["k16"]
-    kq = lambda t: t.repeat_interleave(grp, dim=1)  # noqa: E731  KV head of each query head
-    # the selector's score, recomputed here: its lists must be the library's
-    qbar, kbar = pooled_means(q16), pooled_means(k16)
-    score = sequential_scores(qbar, kq(kbar))
-    idx, n16 = lists_from_mask(select_mask(score, frac))
-    same = bool(torch.equal(idx, lib_idx) and torch.equal(n16, lib_n16))
-    run("pooled_mean", idx, n16)
-    out[-1]["equals_library"] = same
-    del lib_idx, lib_n16, score
-    # max-pooled and exact block max, one head at a time
-    mp = torch.empty((B, Hq, nb, nb), dtype=torch.float64, device=dev)
-    bm = torch.empty((B, Hq, nb, nb), dtype=torch.float64, device=dev)
-    for b in range(B):
-        for h in range(Hq):
-            kh = k16[b, h // grp].float()
-            mp[b, h] = torch.matmul(qbar[b, h].double(), kh.double().t().contiguous()).view(nb, nb, 64).amax(-1)
-            for r0 in range(0, Nn, 4096):
-                r1 = min(Nn, r0 + 4096)
-                s_ = torch.matmul(q16[b, h, r0:r1].float(), kh.t().contiguous())
-                bm[b, h, r0 // 64:r1 // 64] = s_.view((r1 - r0) // 64, 64, nb, 64).amax(dim=(1, 3)).double()
-    run("max_pooled", *lists_from_mask(select_mask(mp, frac)))
-    run("block_max", *lists_from_mask(select_mask(bm, frac)))
-    del mp, bm
-    # norm-weighted means
-    def nw_means(x16):
-        xf = x16.float().view(*x16.shape[:-2], nb, 64, d)
-        wgt = torch.linalg.vector_norm(xf, dim=-1, keepdim=True)
-        return ((xf * wgt).sum(-2) / wgt.sum(-2).clamp_min(1e-30)).float()
-
-    run("norm_weighted", *lists_from_mask(select_mask(sequential_scores(nw_means(q16), kq(nw_means(k16))), frac)))
-    # 128-row blocks
-    if nb % 2 == 0:
-        s128 = sequential_scores(pooled_means(q16, 128), kq(pooled_means(k16, 128)))
-        run("pooled_mean_128", *lists_from_mask(expand_mask(select_mask(s128, frac), 2)))
+    # each block score through the library's selection (thrift_select for the
+    # pooled mean, thrift_select_ex for the others), timed alone
+    sws = torch.empty(binding.lib().thrift_select_workspace_bytes(binding.make_shape(B, Hq, Hkv, Nn, d)),
+                      dtype=torch.uint8, device=dev)
+    for name in ("pooled_mean", "max_pooled", "norm_weighted", "block_max"):
+        idx, n16 = binding.select(qz["q16"], qz["k16"], frac, True, workspace=sws, score=name)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        binding.select(qz["q16"], qz["k16"], frac, True, workspace=sws, idx=idx, n16=n16, score=name)
+        e1.record()
+        torch.cuda.synchronize()
+        run(name, idx, n16, select_ms=round(e0.elapsed_time(e1), 4))
+        del idx, n16
     for r in out:
         r["seconds"] = round(time.perf_counter() - t0, 2)
     return out

@@ -26,8 +26,10 @@
  *     a HIP launch error (hipGetLastError after the launch).
  *   - Shapes: B, Hq, Hkv, N > 0; Hq % Hkv == 0 (query head h reads KV head
  *     floor(h * Hkv / Hq)); d in {64, 128}; block == 64; N % 64 == 0;
- *     causal in {0, 1}; otherwise THRIFT_EINVAL (bad values) or
- *     THRIFT_EUNSUPPORTED (valid but not built: other d, block, N % 64 != 0).
+ *     causal in {0, 1}; N / 64 <= 8192 and B * Hq * N / 64 < 2^24 (one
+ *     workgroup per query block and head); otherwise THRIFT_EINVAL (bad
+ *     values) or THRIFT_EUNSUPPORTED (valid but not built: other d, block,
+ *     N % 64 != 0, beyond those sizes).
  *   - Inputs must be finite with |x| <= 65504; other values give undefined
  *     output but no out-of-bounds access.
  *   - nb = N / 64 blocks.  MXFP4 = OCP MX: E2M1 codes (sign bit 3, element
@@ -55,6 +57,15 @@ typedef enum {
 } thrift_status;
 
 typedef enum { THRIFT_F16 = 0, THRIFT_BF16 = 1, THRIFT_F32 = 2 } thrift_dtype;
+
+/* Block scores for the selection heuristic (thrift_select uses the pooled
+ * mean; the others are the variants of thrift_select_ex). */
+typedef enum {
+  THRIFT_SCORE_POOLED_MEAN = 0,   /* pooled Q mean . pooled K mean */
+  THRIFT_SCORE_MAX_POOLED = 1,    /* max over the key block's rows r of (pooled Q mean . k_r) */
+  THRIFT_SCORE_NORM_WEIGHTED = 2, /* means with each row weighted by its L2 norm */
+  THRIFT_SCORE_BLOCK_MAX = 3      /* largest exact q . k of the block pair (needs all of Q K^T) */
+} thrift_score;
 
 /* Problem statement: batch, query heads, KV heads, tokens, head dim, block
  * size (must be 64), causal mask flag. */
@@ -118,6 +129,39 @@ int64_t thrift_list_entries(const thrift_shape *s);
  */
 int thrift_select(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx,
                   int32_t *n16, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * thrift_select with another block score (the heuristic is the method's open
+ * risk: the hotpaper.ai summary of "ThriftAttention: Selective Mixed
+ * Precision for Long-Context FP4 Attention", section on significance and
+ * limits).  score is a thrift_score; THRIFT_SCORE_POOLED_MEAN gives exactly
+ * thrift_select's lists.  The budget rule, the forced blocks, the ranking
+ * (score descending, lower block index first) and the list layout are those
+ * of thrift_select.  Every score is an fp64 chain over the channels in order
+ * (products of fp32 means and fp16 values are exact), so the lists are
+ * reproducible bit for bit:
+ *   MAX_POOLED     sigma(i,j) = max_r sum_c qbar_i[c] k16[64j + r][c];
+ *   NORM_WEIGHTED  the pooled score of norm-weighted means: row r of a block
+ *                  weighs w_r = sqrt(fma chain of x_rc^2 over c), the mean is
+ *                  (fma chain over r of w_r x_rc) / (sum over r of w_r),
+ *                  rounded to fp32 (0 for an all-zero block);
+ *   BLOCK_MAX      sigma(i,j) = max over the 64 x 64 row pairs of q . k (64^2
+ *                  times the dot products of the pooled score: a comparator).
+ * workspace: thrift_select_workspace_bytes(s) bytes (the means).
+ * Errors: those of thrift_select, THRIFT_EINVAL for an unknown score.
+ */
+int thrift_select_ex(const thrift_shape *s, double frac, int score, const void *q16, const void *k16, int32_t *idx,
+                     int32_t *n16, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The block scores thrift_select_ex ranks, without the selection: scores
+ * (fp32, thrift_list_entries(s) entries) receives sigma(i, j) rounded to fp32
+ * for every valid block pair, at the list layout's positions (row i at
+ * i(i+1)/2 causal or i*nb, entry j).  For studies of the heuristic.
+ * Errors: as thrift_select_ex.
+ */
+int thrift_block_scores(const thrift_shape *s, int score, const void *q16, const void *k16, float *scores,
+                        void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * thrift_select for callers that cannot allocate device memory (code under

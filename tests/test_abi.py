@@ -53,6 +53,16 @@ def sel(L, s, frac=0.05, ptrs=None, ws=FAKE, wsb=1 << 40):
     return L.thrift_select(ctypes.byref(s), frac, *ptrs, ws, wsb, None)
 
 
+def sel_ex(L, s, frac=0.05, score=1, ptrs=None, ws=FAKE, wsb=1 << 40):
+    ptrs = ptrs or [FAKE] * 4
+    return L.thrift_select_ex(ctypes.byref(s), frac, score, *ptrs, ws, wsb, None)
+
+
+def scores_call(L, s, score=0, ptrs=None, ws=FAKE, wsb=1 << 40):
+    ptrs = ptrs or [FAKE] * 3
+    return L.thrift_block_scores(ctypes.byref(s), score, *ptrs, ws, wsb, None)
+
+
 def sel_noalloc(L, s, frac=0.05, ptrs=None):
     ptrs = ptrs or [FAKE] * 4
     return L.thrift_select_noalloc(ctypes.byref(s), frac, *ptrs, None)
@@ -74,12 +84,15 @@ def attn(L, s, out_dtype=2, ptrs=None, lse=None, sm=0.0, ws=FAKE, wsb=1 << 40):
     (dict(B=0), EINVAL), (dict(Hq=0), EINVAL), (dict(Hkv=-1), EINVAL), (dict(N=0), EINVAL),
     (dict(Hq=6, Hkv=4), EINVAL), (dict(causal=2), EINVAL), (dict(d=96), EUNSUP), (dict(d=256), EUNSUP),
     (dict(block=128), EUNSUP), (dict(block=0), EINVAL), (dict(N=1000), EUNSUP), (dict(N=64 * 8193), EUNSUP),
+    (dict(B=2048, Hq=1024, Hkv=1024, N=512), EUNSUP),  # B * Hq * N/64 = 2^24 query-block workgroups
 ])
 def test_bad_shapes(L, kw, code):
     s = shape(**kw)
     assert quant(L, s) == code
     assert sel(L, s) == code
     assert sel_noalloc(L, s) == code
+    assert sel_ex(L, s) == code
+    assert scores_call(L, s) == code
     assert attn(L, s) == code
     assert L.thrift_select_workspace_bytes(ctypes.byref(s)) == 0
     assert L.thrift_attn_workspace_bytes(ctypes.byref(s)) == 0
@@ -140,6 +153,11 @@ def test_workspace(L):
     assert attn(L, s, ws=None) == EWS
     assert attn(L, s, wsb=need_a - 1) == EWS
     assert attn(L, s, ws=ctypes.c_void_p(0x10004), wsb=need_a) == EINVAL
+
+
+def test_largest_grid_is_accepted(L):
+    s = shape(B=2047, Hq=1024, Hkv=1024, N=512)  # 2^24 - 8192 query-block workgroups
+    assert L.thrift_list_entries(ctypes.byref(s)) == 2047 * 1024 * 8 * 9 // 2
 
 
 def test_list_entries(L):
@@ -244,3 +262,24 @@ def test_noalloc_select_size_limit(L):
     too_big = shape(B=2, Hq=32, Hkv=8, N=131072, d=128)
     assert L.thrift_select_workspace_bytes(ctypes.byref(too_big)) > 64 << 20
     assert sel_noalloc(L, too_big) == EWS
+
+
+def test_select_ex_and_block_scores_validation(L):
+    s = shape()
+    for score in (-1, 4):
+        assert sel_ex(L, s, score=score) == EINVAL
+        assert scores_call(L, s, score=score) == EINVAL
+    for f in (-0.01, 1.0001, math.nan):
+        assert sel_ex(L, s, frac=f) == EINVAL
+    for slot in range(4):
+        for bad in (None, ctypes.c_void_p(0x10008)):
+            p = [FAKE] * 4
+            p[slot] = bad
+            assert sel_ex(L, s, ptrs=p) == EINVAL
+            if slot < 3:
+                assert scores_call(L, s, ptrs=p[:3]) == EINVAL
+    need = L.thrift_select_workspace_bytes(ctypes.byref(s))
+    assert sel_ex(L, s, ws=None) == EWS and sel_ex(L, s, wsb=need - 1) == EWS
+    assert scores_call(L, s, ws=None) == EWS and scores_call(L, s, wsb=need - 1) == EWS
+    assert L.thrift_select_ex(None, 0.1, 0, *[FAKE] * 4, FAKE, 1 << 40, None) == EINVAL
+    assert L.thrift_block_scores(None, 0, *[FAKE] * 3, FAKE, 1 << 40, None) == EINVAL
