@@ -24,7 +24,8 @@ Parity status per function:
                                 attention, closed forms, split-merge);
                                 rowsum="weights": V = 1 gives O = 1 exactly,
                                 frac=1 against textbook attention, split-merge,
-                                closed forms
+                                closed forms; rowsum="log": the same, plus
+                                log_encode against a brute-force code search
 """
 from __future__ import annotations
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_select.restype = i32
         L.oracle_select_kind.argtypes = [i32] * 7 + [f64] + [P] * 7
         L.oracle_select_kind.restype = i32
+        L.oracle_log_encode.argtypes = [P, i64, f64, P, P]
+        L.oracle_log_encode.restype = None
         L.oracle_normw_pool.argtypes = [P, i64, i32, i32, P]
         L.oracle_normw_pool.restype = None
         L.oracle_attn_rows.argtypes = [i32] * 6 + [f32] + [P] * 9 + [P, P, P, i64, P, P, P, P, P, P, i32]
@@ -111,6 +114,16 @@ def mx_encode(groups: np.ndarray):
     codes = np.empty(g.shape, dtype=np.uint8)
     scales = np.empty(g.shape[0], dtype=np.uint8)
     lib().oracle_mx_encode(_p(g), g.shape[0], _p(codes), _p(scales))
+    return codes, scales
+
+
+def log_encode(x: np.ndarray, M: float):
+    """Exp-free encoding of rows of 32 scores (log2 units, -inf = masked)
+    against the integer max M -> (codes uint8 [G,32], scale bytes uint8 [G])."""
+    g = _c(x, np.float64).reshape(-1, 32)
+    codes = np.empty(g.shape, dtype=np.uint8)
+    scales = np.empty(g.shape[0], dtype=np.uint8)
+    lib().oracle_log_encode(_p(g), g.shape[0], float(M), _p(codes), _p(scales))
     return codes, scales
 
 
@@ -190,7 +203,7 @@ def row_lists(sel: dict, B, Hq, N, causal, b, h, i):
     return row[:c], row[c:]
 
 
-ROWSUM = {"p": 0, "weights": 1}
+ROWSUM = {"p": 0, "weights": 1, "log": 2}
 
 
 def attn_rows(qz: dict, sel: dict, rows, causal: bool = True, sm_scale: float = 0.0, blk_keep=None,
@@ -198,7 +211,9 @@ def attn_rows(qz: dict, sel: dict, rows, causal: bool = True, sm_scale: float = 
     """Mixed-precision attention for the flat output rows ((b*Hq + h)*N + t).
 
     rowsum "p": the row sum adds the unquantized p; "weights": it adds the
-    weights the P.V products use (fp16(p), dequantized MXFP4 P).
+    weights the P.V products use (fp16(p), dequantized MXFP4 P); "log": as
+    "weights", with FP4 P codes from a piecewise-linear 2^y of the scores
+    (no exponential on FP4 tiles).
     Returns out [R,d] (normalised), lse [R], acc [R,d] (unnormalised), l [R], m [R]."""
     q16 = qz["q16"]
     B, Hq, N, d = q16.shape

@@ -143,6 +143,35 @@ static uint8_t mx_encode_group(const double *v, int n, uint8_t *codes) {
 
 static double e8m0_value(uint8_t s) { return ldexp(1.0, (int)s - 127); }
 
+/*
+ * The exp-free encoding of one 32-key group of P (the other row-sum reading's
+ * cheap FP4 path): x[e] are the keys' scores in log2 units (-inf for a masked
+ * key), M the row's integer running max.  The group exponent follows the MX
+ * rule applied to the largest p = 2^(xmax - M) without forming it:
+ * e = clamp(floor(xmax - M) - 2, -127, 127).  Each key's code is the E2M1
+ * rounding (nearest-even, saturating) of a piecewise-linear stand-in for
+ * 2^y, y = x - M - e: 2^floor(y) * (1 + y - floor(y)), which agrees with 2^y
+ * at integers and is at most 6.1% above it in between; y <= -127 gives 0.
+ * No exponential is taken.  Returns the scale byte.
+ */
+static uint8_t log_encode_group(const double *x, double M, uint8_t *codes) {
+  double xmax = -INFINITY;
+  for (int k = 0; k < 32; k++)
+    if (x[k] > xmax) xmax = x[k];
+  int e = (xmax == -INFINITY) ? -127 : (int)floor(xmax - M) - 2;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  for (int k = 0; k < 32; k++) {
+    double y = x[k] - M - e, z = 0.0;
+    if (y > -127.0) {
+      double f = floor(y);
+      z = ldexp(1.0 + (y - f), (int)f);
+    }
+    codes[k] = (uint8_t)e2m1_magnitude_code(z);
+  }
+  return (uint8_t)(e + 127);
+}
+
 /* packed nibble accessors: element 2j in the low nibble of byte j */
 static int nib(const uint8_t *p, int64_t i) { return (p[i >> 1] >> ((i & 1) * 4)) & 15; }
 
@@ -220,6 +249,12 @@ int oracle_quantize(int B, int Hq, int Hkv, int N, int d, int in_dtype, const ui
     }
   }
   return ORC_OK;
+}
+
+/* The exp-free group encoding above, for ngroups groups of 32 scores (log2
+ * units) against the integer max M: codes [ngroups, 32], scale bytes. */
+void oracle_log_encode(const double *x, int64_t ngroups, double M, uint8_t *codes, uint8_t *scales) {
+  for (int64_t g = 0; g < ngroups; g++) scales[g] = log_encode_group(x + 32 * g, M, codes + 32 * g);
 }
 
 /* ------------------------------------------------------------------ */
@@ -438,7 +473,9 @@ int oracle_select(int B, int Hq, int Hkv, int N, int d, int causal, double frac,
  *   1  the weights the P.V products actually use: fp16(p) on FP16 tiles and
  *      the dequantized MXFP4 code of p on FP4 tiles, so the output is a
  *      convex combination of V rows with exactly those weights (the
- *      alternative reading: normalisation by the quantized weights).
+ *      alternative reading: normalisation by the quantized weights);
+ *   2  as 1, with the FP4 tiles' P codes taken without an exponential
+ *      (log_encode_group): the exp-free FP4 path this reading allows.
  * acc and (for rowsum 1) l take the same terms in the same order.
  *
  * v16 here is [B,Hkv,N,d] (token-major).
@@ -449,7 +486,7 @@ int oracle_attn_rows(int B, int Hq, int Hkv, int N, int d, int causal, float sm_
                      const int32_t *idx, const int32_t *n16, const int64_t *rows, int64_t nrows,
                      const uint8_t *blk_keep, double *out, double *lse, double *acc_out, double *l_out,
                      double *m_out, int rowsum) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N % 64 || d % 32 || rowsum < 0 || rowsum > 1) return ORC_EINVAL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N % 64 || d % 32 || rowsum < 0 || rowsum > 2) return ORC_EINVAL;
   int nb = N / 64;
   int64_t per = causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
   /* score scale in log2 units: c = fl32(sm_scale * log2(e)), sm_scale <= 0 -> fl32(1/sqrt(d)) */
@@ -527,16 +564,23 @@ int oracle_attn_rows(int B, int Hq, int Hkv, int N, int d, int causal, float sm_
             int64_t key = (int64_t)j * 64 + kk;
             if (!live[key]) continue;
             double p16 = half_bits_to_double(double_to_half_bits(p[key]));
-            if (rowsum == 1) l += p16;
+            if (rowsum >= 1) l += p16;
             for (int ch = 0; ch < d; ch++) acc[ch] += p16 * half_bits_to_double(v16[(kvh * N + key) * d + ch]);
           }
         } else if (prec[j] == 4) {
           for (int grp = 0; grp < 2; grp++) {
             int64_t k0 = (int64_t)j * 64 + 32 * grp;
-            uint8_t pc[32];
-            /* masked keys enter the group as zeros */
-            uint8_t ps = mx_encode_group(p + k0, 32, pc);
-            if (rowsum == 1) {
+            uint8_t pc[32], ps;
+            if (rowsum == 2) {
+              /* exp-free codes from the scores; masked keys enter as -inf */
+              double xg[32];
+              for (int e = 0; e < 32; e++) xg[e] = live[k0 + e] ? x[k0 + e] : -INFINITY;
+              ps = log_encode_group(xg, M, pc);
+            } else {
+              /* masked keys enter the group as zeros */
+              ps = mx_encode_group(p + k0, 32, pc);
+            }
+            if (rowsum >= 1) {
               double gw = 0.0; /* exact group sum of the codes' values */
               for (int e = 0; e < 32; e++) gw += e2m1_value(pc[e]);
               l += e8m0_value(ps) * gw;

@@ -39,6 +39,9 @@ MISTAKES = [
     ("norm weights squared", "w[r] = sqrt(ss);", "w[r] = ss;"),
     ("norm-weighted mean divided by the row count", "(float)(acc / wsum)", "(float)(acc / 64.0)"),
     ("block max misses the last query row", "for (int a = 0; a < 64; a++)", "for (int a = 0; a < 63; a++)"),
+    ("exp-free codes: stand-in without the leading 1", "z = ldexp(1.0 + (y - f), (int)f);", "z = ldexp(y - f, (int)f);"),
+    ("exp-free codes: group exponent off by one", "(int)floor(xmax - M) - 2;", "(int)floor(xmax - M) - 1;"),
+    ("exp-free reading falls back to exact codes", "if (rowsum == 2) {", "if (rowsum == 3) {"),
 ]
 CONTROL = ("control: no change in meaning", "l += p[key];", "l += 1.0 * p[key];")
 

@@ -616,3 +616,86 @@ def test_variant_lists_keep_the_selector_invariants(orc):
                     assert len(l16) == expected_budget(frac, i + 1, i)
                     if frac > 0:
                         assert 0 in l16 and i in l16
+
+
+# ------------------------------------------ exp-free FP4 P (the weights reading's cheap path)
+
+
+def brute_force_code(z):
+    """Nearest E2M1 magnitude code to z >= 0, ties to the even code, saturating."""
+    d = np.abs(E2M1[None, :] - np.asarray(z, dtype=np.float64)[..., None])
+    best = d.min(-1, keepdims=True)
+    cand = np.where(d == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(-1)
+    return np.where(even < 99, even, cand.min(-1))
+
+
+def test_log_encoder_against_brute_force(orc):
+    g = np.random.default_rng(61)
+    x = g.normal(0.0, 6.0, size=(4000, 32))
+    x[::7, 5] = -np.inf  # masked keys
+    x[3] = -np.inf  # an all-masked group
+    for M in (0.0, 3.0, -5.0, 40.0):
+        codes, scales = orc.log_encode(x, M)
+        xm = x.max(-1)
+        e = np.where(np.isfinite(xm), np.floor(xm - M) - 2, -127)
+        e = np.clip(e, -127, 127)
+        y = x - M - e[:, None]
+        f = np.floor(np.where(np.isfinite(y), y, 0.0))
+        z = np.where(y > -127, np.ldexp(1.0 + (y - f), f.astype(int)), 0.0)
+        assert np.array_equal(scales, (e + 127).astype(np.uint8))
+        assert np.array_equal(codes, brute_force_code(z).astype(np.uint8))
+
+
+def test_log_encoder_is_exact_at_integer_exponents(orc):
+    # integer y: the stand-in equals 2^y, so the codes are the MX codes of
+    # p = 2^(x - M) themselves
+    g = np.random.default_rng(62)
+    x = g.integers(-20, 6, size=(500, 32)).astype(np.float64)
+    codes, scales = orc.log_encode(x, 2.0)
+    mx_codes, mx_scales = orc.mx_encode(np.exp2(x - 2.0))
+    assert np.array_equal(codes, mx_codes) and np.array_equal(scales, mx_scales)
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.3])
+def test_log_rowsum_fp4_exact_inputs_equal_textbook_attention(orc, frac):
+    # integer scores with c = 1: every y is an integer, so the exp-free codes
+    # are exact and the output is textbook attention
+    q, k, v = fp4_exact_inputs(23)
+    ln2 = float(np.float32(np.log(2.0)))
+    qz = orc.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "fp16")
+    sel = orc.select(qz["q16"], qz["k16"], frac, True)
+    res = orc.attn_rows(qz, sel, orc.all_rows(1, 2, 256), True, ln2, rowsum="log")
+    want = softmax_attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), True, sm_scale=1 / np.log2(np.e))
+    np.testing.assert_allclose(res["out"].reshape(want.shape), want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.05, 1.0])
+def test_log_rowsum_constant_values_give_exactly_one(orc, frac):
+    q, k, _ = synth.random_qkv(1, 2, 1, 512, 64, "bf16", seed=63, scale=1.5)
+    v = torch.ones((1, 1, 512, 64), dtype=torch.bfloat16)
+    qz = orc.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "bf16")
+    sel = orc.select(qz["q16"], qz["k16"], frac, True)
+    res = orc.attn_rows(qz, sel, orc.all_rows(1, 2, 512), rowsum="log")
+    assert np.array_equal(res["out"], np.ones_like(res["out"]))
+
+
+def test_log_rowsum_split_merge_and_closeness_to_the_weights_reading(orc):
+    q, k, v = synth.random_qkv(1, 2, 1, 1024, 64, "bf16", seed=67, scale=2.0)
+    qz = orc.quantize(synth.bits(q), synth.bits(k), synth.bits(v), "bf16")
+    sel = orc.select(qz["q16"], qz["k16"], 0.0, True)
+    rows = np.arange(2 * 1024)
+    one = orc.attn_rows(qz, sel, rows, rowsum="log")
+    g = np.random.default_rng(3)
+    lab = g.integers(0, 3, size=16)
+    st = [orc.attn_rows(qz, sel, rows, blk_keep=(lab == p_), rowsum="log") for p_ in g.permutation(3)]
+    M = np.full(rows.size, -np.inf)
+    for s_ in st:
+        M = np.maximum(M, s_["m"])
+    acc = sum(np.where(np.isfinite(s_["m"])[:, None], s_["acc"] * np.exp2(s_["m"] - M)[:, None], 0) for s_ in st)
+    l = sum(np.where(np.isfinite(s_["m"]), s_["l"] * np.exp2(s_["m"] - M), 0) for s_ in st)
+    assert np.abs(acc / l[:, None] - one["out"]).max() <= 1e-12 * np.abs(one["out"]).max()
+    # the stand-in moves a code by at most one step: the output stays close
+    # to the exact-code weights reading
+    w = orc.attn_rows(qz, sel, rows, rowsum="weights")
+    assert 0 < np.abs(one["out"] - w["out"]).max() < 0.25 * np.abs(w["out"]).max()
