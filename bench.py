@@ -30,7 +30,9 @@ Prints one JSON line:
   alt_rowsum_weights  the attention call under the other row-sum reading
              (thrift_attn_fwd_wsum: normalised by the quantized weights, the
              FP4 row sums from one more MFMA), timed alone over the same
-             steps, with its own quality figures.
+             steps, with its own quality figures;
+  alt_rowsum_weights_expfree  the same reading with FP4 P codes taken
+             without an exponential (thrift_attn_fwd_ex, rowsum 2).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--frac F]
 """
@@ -270,30 +272,36 @@ def main():
                          "frac": round(VALU_SLOTS_PER_FP4_SCORE * (F4 / (4 * w.d)) / (t_f4 * 1e-3) / 1e12 / PEAK_VALU, 4),
                          "fp4_scores": F4 / (4 * w.d), "slots_per_score": VALU_SLOTS_PER_FP4_SCORE},
     }
+    alt = (("alt_rowsum_weights", "weights", "thrift_attn_fwd_wsum"),
+           ("alt_rowsum_weights_expfree", "log", "thrift_attn_fwd_ex rowsum 2"))
     if not args.no_alt:
-        # the same attention call normalised by the quantized weights
-        # (thrift_attn_fwd_wsum), timed alone on the same lists and inputs
-        for _ in range(2):
-            binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws, rowsum="weights")
-        torch.cuda.synchronize()
-        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ea.record()
-        for _ in range(args.steps):
-            binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws, rowsum="weights")
-        eb.record()
-        torch.cuda.synchronize()
-        t_w = ea.elapsed_time(eb) / args.steps
-        result["alt_rowsum_weights"] = {
-            "entry": "thrift_attn_fwd_wsum", "attn_ms": round(t_w, 4),
-            "attn_TFLOPs": round(F / (t_w * 1e-3) / 1e12, 2), "roofline_frac": round(F / (t_w * 1e-3) / 1e12 / peak, 4)}
-        log(f"attention normalised by the quantized weights: {t_w:.3f} ms")
+        # the same attention call under the other row-sum reading: normalised
+        # by the quantized weights (thrift_attn_fwd_wsum), and the same with
+        # exp-free FP4 codes; each timed alone on the same lists and inputs,
+        # with the FP4 kernel's own time from the call's events
+        for key, rs, entry in alt:
+            for _ in range(2):
+                binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws, rowsum=rs)
+            torch.cuda.synchronize()
+            aev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+            for i in range(args.steps):
+                binding.attn_fwd(qz, idx, n16, True, out=out, workspace=aws, rowsum=rs, events=aev[i])
+            torch.cuda.synchronize()
+            t_w = sum(e[0].elapsed_time(e[3]) for e in aev) / args.steps
+            t_w4 = sum(e[1].elapsed_time(e[2]) for e in aev) / args.steps
+            result[key] = {
+                "entry": entry, "attn_ms": round(t_w, 4), "attn_fwd_kernel_ms": round(t_w4, 4),
+                "attn_TFLOPs": round(F / (t_w * 1e-3) / 1e12, 2),
+                "roofline_frac": round(F / (t_w * 1e-3) / 1e12 / peak, 4)}
+            log(f"attention, row-sum reading {rs}: {t_w:.3f} ms (FP4 kernel {t_w4:.3f} ms)")
     if not args.no_quality:
         result["quality"] = quality(binding, torch, qz, w, x["needles"], frac, dev)
         log(f"quality {result['quality']}")
         if not args.no_alt:
             from fp16_long_context_amd.quality import errors
 
-            result["alt_rowsum_weights"]["quality"] = errors(binding, torch, qz, w, x["needles"], frac, "weights")
+            for key, rs, _ in alt:
+                result[key]["quality"] = errors(binding, torch, qz, w, x["needles"], frac, rs)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, w, frac)
         log(f"cpu baseline {result['cpu_baseline']['value']:.3e} TFLOP/s on {result['cpu_baseline']['cores']} threads")

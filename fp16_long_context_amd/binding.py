@@ -251,6 +251,12 @@ def select_noalloc(q16: torch.Tensor, k16: torch.Tensor, frac: float, causal: bo
     return idx, n16
 
 
+# row-sum readings of the attention call: "p" (thrift_attn_fwd), "weights"
+# (thrift_attn_fwd_wsum), "log" (the weights reading with exp-free FP4 codes,
+# thrift_attn_fwd_ex rowsum 2)
+ROWSUM = {"p": 0, "weights": 1, "log": 2}
+
+
 def attn_workspace_bytes(B, Hq, Hkv, N, d, causal=True) -> int:
     s = make_shape(B, Hq, Hkv, N, d, causal)
     return int(lib().thrift_attn_workspace_bytes(ctypes.byref(s)))
@@ -262,11 +268,13 @@ def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True
     """Fused FP16/MXFP4 attention.  Returns (out [B,Hq,N,d], lse [B,Hq,N] or None).
     out, lse and the workspace (uint8, thrift_attn_workspace_bytes) may be preallocated.
     rowsum "p" (thrift_attn_fwd): the row sum adds the unquantized p;
-    "weights" (thrift_attn_fwd_wsum): it adds the weights the P.V products use.
+    "weights" (thrift_attn_fwd_wsum): it adds the weights the P.V products use;
+    "log" (thrift_attn_fwd_ex, rowsum 2): as "weights", with FP4 P codes taken
+    without an exponential.
     events: optional four torch.cuda.Event(enable_timing=True), recorded on the
     current stream before, between and after the three kernels (thrift_attn_fwd_ex)."""
-    if rowsum not in ("p", "weights"):
-        raise ThriftError("rowsum must be 'p' or 'weights'")
+    if rowsum not in ROWSUM:
+        raise ThriftError(f"rowsum must be one of {sorted(ROWSUM)}")
     q16 = qz["q16"]
     if q16.dim() != 4 or qz["k16"].dim() != 4:
         raise ThriftError("q16/k16 must be 4-D")
@@ -300,15 +308,17 @@ def attn_fwd(qz: dict, idx: torch.Tensor, n16: torch.Tensor, causal: bool = True
             *[_ptr(qz[n]) for n in ("q16", "k16", "v16", "q4", "q4s", "k4", "k4s", "v4", "v4s")],
             _ptr(idx), _ptr(n16), _ptr(out), _DT[out.dtype], _ptr(lse), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(q16.device)]
-    if events is None:
+    if events is None and rowsum != "log":
         rc = (L.thrift_attn_fwd if rowsum == "p" else L.thrift_attn_fwd_wsum)(*args)
     else:
-        if len(events) != 4:
-            raise ThriftError("events must hold four torch.cuda.Event")
-        for e in events:  # make sure each event exists on the device
-            e.record()
-        evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
-        rc = L.thrift_attn_fwd_ex(*args, 0 if rowsum == "p" else 1, evs)
+        evs = None
+        if events is not None:
+            if len(events) != 4:
+                raise ThriftError("events must hold four torch.cuda.Event")
+            for e in events:  # make sure each event exists on the device
+                e.record()
+            evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        rc = L.thrift_attn_fwd_ex(*args, ROWSUM[rowsum], evs)
     _check(rc, "thrift_attn_fwd")
     return out, lse
 

@@ -206,7 +206,7 @@ int thrift_attn_fwd_ex(const thrift_shape *s, float sm_scale, const void *q16, c
                        const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
                        float *lse, void *workspace, size_t ws_bytes, void *stream, int rowsum,
                        void *const *events) {
-  if (rowsum != 0 && rowsum != 1) return THRIFT_EINVAL;
+  if (rowsum < 0 || rowsum > 2) return THRIFT_EINVAL;
   return attn_fwd_common(s, sm_scale, q16, k16, v16, q4, q4s, k4, k4s, v4, v4s, idx, n16, out, out_dtype, lse,
                          workspace, ws_bytes, stream, rowsum, events);
 }

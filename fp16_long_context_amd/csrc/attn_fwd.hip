@@ -176,6 +176,27 @@ __device__ __forceinline__ float lane_max32(const float16v (&s)[2]) {
   return fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
 }
 
+// Raise the integer running max M (log2 units) to ceil(row max * c) when it
+// exceeds M by more than kLazy (or M is still -inf), rescaling acc and the
+// row sum by the exact power of two.  lane_max: this lane's largest raw
+// score (the row's other 32 keys sit in lane l ^ 32).
+template <int CB>
+__device__ __forceinline__ void raise_max(const float lane_max, float16v (&acc)[CB], float &M, float &l_part,
+                                          const float c) {
+  const float row_max = fmaxf(lane_max, other_half(lane_max));
+  const float mt = ceilf(row_max * c);  // integer candidate max (log2 units)
+  const bool raise = (mt > M + kLazy) || (M == -INFINITY);
+  if (__ballot(raise)) {  // wave-uniform; lanes that keep their max scale by 1
+    const float sc = raise ? ((M == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(M - mt))) : 1.0f;
+    M = raise ? mt : M;
+    l_part *= sc;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[cb][r] *= sc;
+  }
+}
+
 // Online-softmax step on one 32-query x 64-key score tile held as s[2]
 // (this lane: query col, keys 32*lh + 0..31).  Applies the causal mask on
 // the diagonal tile, raises the integer running max when needed (rescaling
@@ -195,18 +216,7 @@ __device__ __forceinline__ float softmax_step(float16v (&s)[2], float16v (&acc)[
         if (32 * lh + 16 * blk + r > qpos) s[blk][r] = -INFINITY;
   }
   const float lane_max = lane_max32(s);
-  const float row_max = fmaxf(lane_max, other_half(lane_max));
-  const float mt = ceilf(row_max * c);  // integer candidate max (log2 units)
-  const bool raise = (mt > M + kLazy) || (M == -INFINITY);
-  if (__ballot(raise)) {  // wave-uniform; lanes that keep their max scale by 1
-    const float sc = raise ? ((M == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(M - mt))) : 1.0f;
-    M = raise ? mt : M;
-    l_part *= sc;
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[cb][r] *= sc;
-  }
+  raise_max<CB>(lane_max, acc, M, l_part, c);
   const float negM = -M;
   float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
@@ -375,19 +385,10 @@ __device__ __forceinline__ void fp4_scores(const uint8_t *kst, const uint8_t *vs
   }
 }
 
-// FP4 tile, second half: p (this lane's 32 values, one aligned 32-key group,
-// relative to the max the exponent used) re-quantized to MXFP4, and
-// O^T += V^T P^T.
-// WS 1: also adds the lane's dequantized P to *l_add (VALU); WS 2: also
-// accumulates the dequantized P of every key into lacc with one more scaled
-// MFMA against E2M1 ones (every row of lacc then holds the row's sum).
-template <int CB, int WS = 0>
-__device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
-                                       const int4v (&va)[CB], const int (&vs)[CB], float16v (&acc)[CB],
-                                       float *l_add = nullptr, float16v *lacc = nullptr) {
-  const int psb = mx_scale_byte(amax);
-  const float div = mx_scale_divisor(psb);
-  uint32_t pw[4];
+// The lane's 32 values of s (one aligned 32-key group), divided by div and
+// rounded to E2M1, packed: byte b of word w holds keys 16(w/2) + 8(w%2) +
+// 2b, +1 (low nibble first).
+__device__ __forceinline__ void fp4_pack(const float16v (&s)[2], const float div, uint32_t (&pw)[4]) {
 #pragma unroll
   for (int w = 0; w < 4; w++) {
     const int blk = w >> 1, r0 = 8 * (w & 1);
@@ -399,6 +400,40 @@ __device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 4], s[blk][r0 + 5], div, 2);
     THRIFT_CVT_FP4(pw[w], s[blk][r0 + 6], s[blk][r0 + 7], div, 3);
   }
+}
+
+// Exp-free codes of the lane's 32 raw scores s (the other row-sum reading's
+// cheap FP4 path): the group exponent is the MX rule applied to the largest
+// p = 2^(x_max - M) without forming it, e = floor(x_max - M) - 2 (clamped to
+// [-127, 127]; -127 for an all-masked group), and each key's code is the
+// E2M1 rounding of 2^floor(y) (1 + frac y), y = x - M - e.  That float is
+// the bit pattern (y + 127) 2^23, so one fma (s c 2^23 + (127 - M - e) 2^23)
+// and one saturating conversion to an integer give it; y <= -127 (and a
+// masked -inf) saturate to 0.  Returns the scale byte e + 127; `big` is set
+// when e exceeds the fixed-max walk's limit (p above 2^100).
+__device__ __forceinline__ int fp4_log_codes(float16v (&s)[2], const float M, const float c, uint32_t (&pw)[4],
+                                             bool &big) {
+  const float xm = lane_max32(s) * c;
+  int e = -127;
+  if (xm != -INFINITY) e = min(max((int)floorf(xm - M) - 2, -127), 127);
+  big = e > 98;
+  const float c23 = c * 8388608.0f, k23 = (127.0f - M - (float)e) * 8388608.0f;
+#pragma unroll
+  for (int blk = 0; blk < 2; blk++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) s[blk][r] = __uint_as_float((uint32_t)fmaf(s[blk][r], c23, k23));
+  fp4_pack(s, 1.0f, pw);
+  return e + 127;
+}
+
+// O^T += V^T P^T for the packed codes pw with scale byte psb.  WS 1: also adds
+// the lane's dequantized P to *l_add (VALU); WS 2: also accumulates the
+// dequantized P of every key into lacc with one more scaled MFMA against
+// E2M1 ones (every row of lacc then holds the row's sum).
+template <int CB, int WS = 0>
+__device__ __forceinline__ void fp4_pv_codes(const uint32_t (&pw)[4], const int psb, const int4v (&va)[CB],
+                                             const int (&vs)[CB], float16v (&acc)[CB], float *l_add = nullptr,
+                                             float16v *lacc = nullptr) {
   int8v pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], 0, 0, 0, 0};
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) {
@@ -413,8 +448,23 @@ __device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax,
   }
 }
 
+// FP4 tile, second half: p (this lane's 32 values, one aligned 32-key group,
+// relative to the max the exponent used, amax their largest) re-quantized to
+// MXFP4, and O^T += V^T P^T (WS as fp4_pv_codes).
+template <int CB, int WS = 0>
+__device__ __forceinline__ void fp4_pv(const float16v (&s)[2], const float amax, const int4v (&va)[CB],
+                                       const int (&vs)[CB], float16v (&acc)[CB], float *l_add = nullptr,
+                                       float16v *lacc = nullptr) {
+  const int psb = mx_scale_byte(amax);
+  uint32_t pw[4];
+  fp4_pack(s, mx_scale_divisor(psb), pw);
+  fp4_pv_codes<CB, WS>(pw, psb, va, vs, acc, l_add, lacc);
+}
+
 // One FP4 tile (general walk): the running max may rise, rescaling acc.
-template <int D, int HPW, bool MASK, bool W = false>
+// R: the row-sum reading (0 the unquantized p, 1 the weights P.V uses, 2 as
+// 1 with exp-free P codes).
+template <int D, int HPW, bool MASK, int R = 0>
 __device__ __forceinline__ void tile_fp4(const uint8_t *kst, const uint8_t *vst, const int4v (&qf4)[D / 64], const int (&qs4)[D / 64],
                                          float16v (&acc)[D / 32], float &M, float &l_part, const float c,
                                          const int col, const int lh, const int qpos) {
@@ -423,8 +473,16 @@ __device__ __forceinline__ void tile_fp4(const uint8_t *kst, const uint8_t *vst,
   int4v va[CB];
   int vs[CB];
   fp4_scores<D, HPW, MASK>(kst, vst, qf4, qs4, col, lh, qpos, s, va, vs);
-  const float lane_max = softmax_step<CB, false, W ? 2 : 0>(s, acc, M, l_part, c, lh, qpos);
-  fp4_pv<CB, W ? 1 : 0>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, -M)), va, vs, acc, &l_part);
+  if (R == 2) {
+    raise_max<CB>(lane_max32(s), acc, M, l_part, c);
+    uint32_t pw[4];
+    bool big;
+    const int psb = fp4_log_codes(s, M, c, pw, big);
+    fp4_pv_codes<CB, 1>(pw, psb, va, vs, acc, &l_part);
+  } else {
+    const float lane_max = softmax_step<CB, false, R ? 2 : 0>(s, acc, M, l_part, c, lh, qpos);
+    fp4_pv<CB, R ? 1 : 0>(s, __builtin_amdgcn_exp2f(fmaf(lane_max, c, -M)), va, vs, acc, &l_part);
+  }
 }
 
 // Softmax and P.V of one FP4 tile whose scores s are already computed,
@@ -434,10 +492,19 @@ __device__ __forceinline__ void tile_fp4(const uint8_t *kst, const uint8_t *vst,
 // group scale comes from the largest p of the lane's 32-key group (the MXFP4
 // rule's amax, taken after the exponentials).  A group with amax above kMaxP
 // (or not finite) sets `overflow`.
-template <int CB, bool W = false>
+template <int CB, int R = 0>
 __device__ __forceinline__ void fp4_fixed_rest(float16v (&s)[2], const int4v (&va)[CB], const int (&vs)[CB],
                                                float16v (&acc)[CB], const float M, float &l_part, bool &overflow,
                                                const float c, float16v *lacc = nullptr) {
+  if (R == 2) {  // exp-free codes; the row sum from the ones-MFMA
+    uint32_t pw[4];
+    bool big;
+    const int psb = fp4_log_codes(s, M, c, pw, big);
+    overflow = overflow || big;
+    fp4_pv_codes<CB, 2>(pw, psb, va, vs, acc, nullptr, lacc);
+    return;
+  }
+  constexpr bool W = R != 0;
   const float negM = -M;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
@@ -465,7 +532,7 @@ __device__ __forceinline__ bool not_finite(float x) { return (__float_as_uint(x)
 // One FP16 tile for one wave: S^T from FP16 K and Q, P rounded to fp16,
 // O^T += V^T P^T with FP16 V.  st16 is the tile's FP16 region (K rows, then
 // channel-major V); qrow16 points at this lane's Q16 row in LDS.
-template <int D, int HPW, bool MASK, bool W = false>
+template <int D, int HPW, bool MASK, int R = 0>
 __device__ __forceinline__ void tile_fp16(const uint8_t *st16, const uint8_t *qrow16, float16v (&acc)[D / 32],
                                           float &M, float &l_part, const float c, const int col_in, const int lh,
                                           const int qpos) {
@@ -503,7 +570,7 @@ __device__ __forceinline__ void tile_fp16(const uint8_t *st16, const uint8_t *qr
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[u], qb[u], s[1], 0, 0, 0);
     }
   }
-  softmax_step<CB, MASK, W ? 1 : 0>(s, acc, M, l_part, c, lh, qpos);
+  softmax_step<CB, MASK, R ? 1 : 0>(s, acc, M, l_part, c, lh, qpos);
   // P in fp16; MFMA u consumes keys 32*lh + 8u + 0..7 of this lane
   half8 pb[4];
 #pragma unroll
@@ -816,8 +883,9 @@ __device__ __forceinline__ void tile_fp16_half(const uint8_t *st16, const half8 
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D, bool W>
+template <int D, int R>
 __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
+  constexpr bool W = R != 0;  // the row sum adds fp16(p)
   using T = Tile<D, 1>;
   constexpr int CB = D / 32;
   constexpr int F = Partial<D>::FIELDS;
@@ -893,35 +961,35 @@ __global__ __launch_bounds__(256) void attn_f16_kernel(AttnArgs a) {
   // Ring of SLOTS FP16 tiles: list entry e in slot e % SLOTS; the loads of
   // entry e + SLOTS - 1 are issued while entry e is computed, and the wait
   // at the end of an entry keeps the newer entries' loads in flight.
-  constexpr int R = Tile16<D>::SLOTS;
+  constexpr int RS = Tile16<D>::SLOTS;  // ring slots
   constexpr int LPT = Loader<D, 4>::NG16;  // load instructions per tile and wave
-  int jq[R];                                // blocks of entries e .. e + R - 1 (-1: none or skipped)
+  int jq[RS];                                // blocks of entries e .. e + RS - 1 (-1: none or skipped)
 #pragma unroll
-  for (int q = 0; q < R; q++) jq[q] = (q < cnt) ? entry(q) : -1;
+  for (int q = 0; q < RS; q++) jq[q] = (q < cnt) ? entry(q) : -1;
 #pragma unroll
-  for (int q = 0; q < R - 1; q++)
+  for (int q = 0; q < RS - 1; q++)
     if (jq[q] >= 0) ld.fp16(lds_addr(smem) + q * T::FP16_BYTES, jq[q]);
   wait_vmem();
   __syncthreads();
-  // One step of the ring: finish entry e (its tile in slot e % R) with the
-  // loads of entry e + R - 1 in flight.
+  // One step of the ring: finish entry e (its tile in slot e % RS) with the
+  // loads of entry e + RS - 1 in flight.
   auto ring_step = [&](const int e, auto tile) {
-    const int jl = jq[R - 1];  // entry e + R - 1
-    if (jl >= 0) ld.fp16(lds_addr(smem) + ((e + R - 1) % R) * T::FP16_BYTES, jl);
-    tile(smem + (e % R) * T::FP16_BYTES, jq[0]);
-    // entry e + 1 must have landed; entries e + 2 .. e + R - 1 may stay in flight
+    const int jl = jq[RS - 1];  // entry e + RS - 1
+    if (jl >= 0) ld.fp16(lds_addr(smem) + ((e + RS - 1) % RS) * T::FP16_BYTES, jl);
+    tile(smem + (e % RS) * T::FP16_BYTES, jq[0]);
+    // entry e + 1 must have landed; entries e + 2 .. e + RS - 1 may stay in flight
     int inflight = 0;
 #pragma unroll
-    for (int q = 2; q < R; q++) inflight += jq[q] >= 0 ? 1 : 0;
-    if (R < 3 || inflight == 0)
+    for (int q = 2; q < RS; q++) inflight += jq[q] >= 0 ? 1 : 0;
+    if (RS < 3 || inflight == 0)
       barrier_vmcnt<0>();
-    else if (R < 4 || inflight == 1)
+    else if (RS < 4 || inflight == 1)
       barrier_vmcnt<LPT>();
     else
       barrier_vmcnt<2 * LPT>();
 #pragma unroll
-    for (int q = 0; q < R - 1; q++) jq[q] = jq[q + 1];
-    jq[R - 1] = (e + R < cnt) ? entry(e + R) : -1;
+    for (int q = 0; q < RS - 1; q++) jq[q] = jq[q + 1];
+    jq[RS - 1] = (e + RS < cnt) ? entry(e + RS) : -1;
   };
   // The list holds distinct blocks in ascending order, so entries before the
   // last are never the diagonal block (the last valid one): one unmasked
@@ -1009,7 +1077,7 @@ __device__ __forceinline__ int *redo_flags(const AttnArgs &a) {
 // (block j in slots j % 2), with tile bodies that raise M whenever a block
 // needs it; then the rows are stored.  Same grid as the FP4 kernel; a
 // workgroup whose item was not flagged returns at once.
-template <int D, int HPW, bool W>
+template <int D, int HPW, int R>
 __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
   using T = Tile<D, HPW>;
   constexpr int KS4 = D / 64, CB = D / 32;
@@ -1072,14 +1140,14 @@ __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
       const uint8_t *s16 = slot16 + sl * T::FP16_BYTES, *ks4 = kslot + sl * T::KSLOT, *vs4 = vslot + sl * T::VSLOT;
       if (a.causal && j == nv - 1) {
         if (fc)
-          tile_fp16<D, HPW, true, W>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
+          tile_fp16<D, HPW, true, R>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
         else
-          tile_fp4<D, HPW, true, W>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+          tile_fp4<D, HPW, true, R>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
       } else {
         if (fc)
-          tile_fp16<D, HPW, false, W>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
+          tile_fp16<D, HPW, false, R>(s16, qrow16, acc, M, l_part, c, col, lh, qpos);
         else
-          tile_fp4<D, HPW, false, W>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+          tile_fp4<D, HPW, false, R>(ks4, vs4, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
       }
     }
     wait_vmem();
@@ -1097,8 +1165,9 @@ __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
 // list, with the FP4 QK product one block ahead.  The walk is the same for
 // all waves (K/V tiles are shared in LDS); a head skips a block of its own
 // FP16 list by adding neither p to l nor P.V to the accumulator.
-template <int D, int HPW, bool W>
+template <int D, int HPW, int R>
 __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
+  constexpr bool W = R != 0;  // the row sum adds the weights P.V uses
   using T = Tile<D, HPW>;
   constexpr int NT = 128 * HPW;                  // threads
   constexpr int KS4 = D / 64;                    // k-steps of the FP4 QK product
@@ -1229,7 +1298,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
     int4v va[CB];
     int vs[CB];
     fp4_vops_at<D, HPW>(k * T::VSLOT, fo, va, vs);
-    fp4_fixed_rest<CB, W>(s, va, vs, acc, M, l_part, overflow, c, &lacc);
+    fp4_fixed_rest<CB, R>(s, va, vs, acc, M, l_part, overflow, c, &lacc);
   };
   // Step at walk position m (slot m % 2): loads the K and V of position m+1
   // into the other slot, then finishes position m if this wave's head has
@@ -1262,7 +1331,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
       wait_vmem();
       __syncthreads();
       if (head_ok && !((hd >> hl) & 1u))
-        tile_fp4<D, HPW, true, W>(kslot, vslot, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
+        tile_fp4<D, HPW, true, R>(kslot, vslot, qf4, qs4, acc, M, l_part, c, col, lh, qpos);
     }
   }
   // An FP4 group above kMaxP, or an accumulator or row sum that left the
@@ -1278,13 +1347,13 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   if (!flagged && head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
 }
 
-template <int D, int HPW, bool W>
+template <int D, int HPW, int R>
 static hipError_t set_fp4_attrs() {
   using T = Tile<D, HPW>;
-  hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW, W>,
+  hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<D, HPW, R>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, T::F4_LDS);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  return hipFuncSetAttribute((const void *)attn_redo_kernel<D, HPW, R>, hipFuncAttributeMaxDynamicSharedMemorySize,
                              T::LDS);
 }
 
@@ -1294,7 +1363,7 @@ static hipError_t set_fp4_attrs() {
 // two-head workgroup idles); then the redo kernels over the same grids.
 // ev (nullable): four caller-created events recorded on st before the FP16
 // kernel, between the kernels and after the redo kernels.
-template <int D, bool W>
+template <int D, int R>
 static hipError_t launch_d(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {
   const int group = a.Hq / a.Hkv;
   const int pairs = group / 2, single = group % 2;
@@ -1308,30 +1377,31 @@ static hipError_t launch_d(const AttnArgs &a, hipStream_t st, hipEvent_t const *
   a1.hspan = single;
   a1.fbase = (int)(per_head * (unsigned)pairs);
   const dim3 grid2(per_head * (unsigned)pairs), grid1(per_head);
-  hipError_t e = hipFuncSetAttribute((const void *)attn_f16_kernel<D, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  constexpr int R16 = R ? 1 : 0;  // FP16 tiles: readings 1 and 2 add fp16(p) alike
+  hipError_t e = hipFuncSetAttribute((const void *)attn_f16_kernel<D, R16>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      Tile16<D>::LDS);
   if (e != hipSuccess) return e;
-  if (pairs && (e = set_fp4_attrs<D, 2, W>()) != hipSuccess) return e;
-  if (single && (e = set_fp4_attrs<D, 1, W>()) != hipSuccess) return e;
+  if (pairs && (e = set_fp4_attrs<D, 2, R>()) != hipSuccess) return e;
+  if (single && (e = set_fp4_attrs<D, 1, R>()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_f16_kernel<D, W>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(256), Tile16<D>::LDS, st, a);
+  hipLaunchKernelGGL((attn_f16_kernel<D, R16>), dim3(nb * (unsigned)(a.B * a.Hq)), dim3(256), Tile16<D>::LDS, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   if (pairs) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, 2, W>), grid2, dim3(256), (Tile<D, 2>::F4_LDS), st, a2);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 2, R>), grid2, dim3(256), (Tile<D, 2>::F4_LDS), st, a2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (single) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, 1, W>), grid1, dim3(128), (Tile<D, 1>::F4_LDS), st, a1);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, 1, R>), grid1, dim3(128), (Tile<D, 1>::F4_LDS), st, a1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   if (pairs) {
-    hipLaunchKernelGGL((attn_redo_kernel<D, 2, W>), grid2, dim3(256), (Tile<D, 2>::LDS), st, a2);
+    hipLaunchKernelGGL((attn_redo_kernel<D, 2, R>), grid2, dim3(256), (Tile<D, 2>::LDS), st, a2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (single) {
-    hipLaunchKernelGGL((attn_redo_kernel<D, 1, W>), grid1, dim3(128), (Tile<D, 1>::LDS), st, a1);
+    hipLaunchKernelGGL((attn_redo_kernel<D, 1, R>), grid1, dim3(128), (Tile<D, 1>::LDS), st, a1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (ev) e = hipEventRecord(ev[3], st);
@@ -1339,8 +1409,12 @@ static hipError_t launch_d(const AttnArgs &a, hipStream_t st, hipEvent_t const *
 }
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t st, hipEvent_t const *ev) {
-  if (a.d == 128) return a.rowsum ? launch_d<128, true>(a, st, ev) : launch_d<128, false>(a, st, ev);
-  return a.rowsum ? launch_d<64, true>(a, st, ev) : launch_d<64, false>(a, st, ev);
+  if (a.d == 128) {
+    if (a.rowsum == 2) return launch_d<128, 2>(a, st, ev);
+    return a.rowsum ? launch_d<128, 1>(a, st, ev) : launch_d<128, 0>(a, st, ev);
+  }
+  if (a.rowsum == 2) return launch_d<64, 2>(a, st, ev);
+  return a.rowsum ? launch_d<64, 1>(a, st, ev) : launch_d<64, 0>(a, st, ev);
 }
 
 size_t attn_workspace_bytes(const int B, const int Hq, const int N, const int d) {

@@ -63,7 +63,8 @@ struct AttnArgs {
   float *lse;
   float *ws;  // partial state of every row after its FP16 blocks
   int B, Hq, Hkv, N, d, causal, out_dtype;
-  int rowsum;  // 0: the row sum adds the unquantized p; 1: the weights P.V uses
+  int rowsum;  // 0: the row sum adds the unquantized p; 1: the weights P.V uses;
+               // 2: as 1, with FP4 P codes taken without an exponential
   float c;     // fl32(sm_scale * log2 e)
   // Set by the attention launcher for each FP4/redo launch: the launch
   // covers heads [hbase, hbase + hspan) of every GQA group, and its

@@ -226,14 +226,20 @@ int thrift_attn_fwd_wsum(const thrift_shape *s, float sm_scale, const void *q16,
                          const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,
                          float *lse, void *workspace, size_t ws_bytes, void *stream);
 
-/* thrift_attn_fwd (rowsum 0) or thrift_attn_fwd_wsum (rowsum 1) with an
- * optional timing hook: events, when not NULL, points at four hipEvent_t
+/* thrift_attn_fwd (rowsum 0), thrift_attn_fwd_wsum (rowsum 1), or (rowsum 2)
+ * the weights reading with an exp-free FP4 path: on FP4 tiles P's group
+ * exponent is the MX rule applied to the group's largest score,
+ * e = floor(x_max - M) - 2, and each key's E2M1 code is the nearest-even
+ * rounding of 2^floor(y) (1 + frac y), y = x - M - e, a piecewise-linear
+ * stand-in for 2^y (equal at integers, at most 6.1% above in between), so
+ * no exponential is taken there; the row sum adds the dequantized codes as
+ * in rowsum 1.  With an optional timing hook: events, when not NULL, points at four hipEvent_t
  * the caller created (as void *); they are recorded on `stream` before the
  * FP16-tile kernel, between it and the FP4-tile kernel launches (two for a
  * GQA group of odd size: its head pairs, then its last head), between those
  * and the overflow-redo launches, and after them, so the caller can time
  * each phase with hipEventElapsedTime.  Errors: those of thrift_attn_fwd, THRIFT_EINVAL
- * for another rowsum, THRIFT_EHIP if an event cannot be recorded. */
+ * for a rowsum outside 0..2, THRIFT_EHIP if an event cannot be recorded. */
 int thrift_attn_fwd_ex(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,
                        const void *q4, const void *q4s, const void *k4, const void *k4s, const void *v4,
                        const void *v4s, const int32_t *idx, const int32_t *n16, void *out, int out_dtype,

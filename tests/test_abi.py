@@ -73,7 +73,7 @@ def attn(L, s, out_dtype=2, ptrs=None, lse=None, sm=0.0, ws=FAKE, wsb=1 << 40):
     ptrs = ptrs or [FAKE] * 12
     codes = {fn(ctypes.byref(s), sm, *ptrs[:11], ptrs[11], out_dtype, lse, ws, wsb, None)
              for fn in (L.thrift_attn_fwd, L.thrift_attn_fwd_wsum)}
-    for rowsum in (0, 1):
+    for rowsum in (0, 1, 2):
         codes.add(L.thrift_attn_fwd_ex(ctypes.byref(s), sm, *ptrs[:11], ptrs[11], out_dtype, lse, ws, wsb, None,
                                        rowsum, None))
     assert len(codes) == 1, codes
@@ -134,7 +134,7 @@ def test_bad_values(L):
 
 def test_attn_ex_rejects_unknown_rowsum(L):
     s = shape()
-    for rowsum in (-1, 2):
+    for rowsum in (-1, 3):
         assert L.thrift_attn_fwd_ex(ctypes.byref(s), 0.0, *[FAKE] * 12, 2, None, FAKE, 1 << 40, None, rowsum,
                                     None) == EINVAL
 

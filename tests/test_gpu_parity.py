@@ -369,3 +369,59 @@ def test_timing_hook_events_and_same_output():
         t = [ev[0].elapsed_time(ev[i]) for i in (1, 2, 3)]
         say(f"[case] timing hook {rowsum}: kernel ends at {t} ms")
         assert 0.0 <= t[0] <= t[1] <= t[2]
+
+
+# --------------------------- exp-free FP4 P under the weights reading (rowsum "log")
+
+
+def test_log_tiny_and_generators():
+    x = synth.generate("tiny")
+    run_case(x["q"], x["k"], x["v"], 0.05, label="tiny", rowsum="log")
+    y = synth.generate("long_128k", N=1024)
+    run_case(y["q"], y["k"], y["v"], 0.05, label="rope@1k", rowsum="log")
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.05, 1.0])
+def test_log_llama_shaped(frac):
+    x = synth.generate("llama8b_16k", N=1024)
+    run_case(x["q"], x["k"], x["v"], frac, label=f"llama8b@1k frac={frac}", rowsum="log")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,dtype,frac", [
+    (2, 14, 2, 512, 128, True, "bf16", 0.05),
+    (1, 4, 2, 512, 64, True, "fp16", 0.3),
+    (1, 3, 3, 320, 128, False, "fp16", 0.3),
+    (1, 2, 1, 64, 128, True, "bf16", 0.05),
+])
+def test_log_shapes(B, Hq, Hkv, N, d, causal, dtype, frac):
+    q, k, v = synth.random_qkv(B, Hq, Hkv, N, d, dtype, seed=B * 1000 + N, scale=1.5)
+    run_case(q, k, v, frac, causal, label="shape", rowsum="log")
+
+
+def test_log_constant_values_give_one():
+    q, k, _ = synth.random_qkv(1, 8, 2, 2048, 128, "bf16", seed=59, scale=1.5)
+    v = torch.ones((1, 2, 2048, 128), dtype=torch.bfloat16)
+    dev = torch.device("cuda:0")
+    qz = binding.quantize(q.to(dev), k.to(dev), v.to(dev))
+    for frac in (0.0, 0.05, 1.0):
+        idx, n16 = binding.select(qz["q16"], qz["k16"], frac)
+        out, _ = binding.attn_fwd(qz, idx, n16, rowsum="log")
+        err = (out - 1.0).abs().max().item()
+        say(f"[case] log V=1 frac={frac}: max|O - 1| = {err:.3e}")
+        assert err < 1e-5
+
+
+@pytest.mark.parametrize("Hq", [4, 3])
+def test_log_redo_walk_on_overflow(Hq):
+    # a planted key far above every FP16 block of its rows: the fixed-max
+    # walk flags the item and the redo walk (exp-free codes too) recomputes it
+    q, k, v = synth.random_qkv(1, Hq, 1, 512, 128, "fp16", seed=77)
+    k[0, 0, 200] = (12.0 * q[0, Hq - 1, 450].float()).to(q.dtype)
+    run_case(q, k, v, 0.0, label=f"redo walk Hq={Hq}", rowsum="log")
+
+
+def test_log_full_size_sampled():
+    x = synth.generate("llama8b_16k")
+    w = x["w"]
+    rows = sample_rows(x, w.B, w.Hq, w.N, 40, 7)
+    run_case(x["q"], x["k"], x["v"], w.frac, rows=rows, label="llama8b_16k", rowsum="log")

@@ -31,7 +31,7 @@ MISTAKES = [
     ("wrong GQA map", "int64_t g = h * Hkv / Hq;", "int64_t g = h % Hkv;"),
     ("budget rounded down", "long long want = (ppm * nv + 999999) / 1000000;", "long long want = (ppm * nv) / 1000000;"),
     ("ranking ascending", "if (a->s > b->s) return -1;", "if (a->s < b->s) return -1;"),
-    ("weights reading: FP16 term unrounded", "if (rowsum == 1) l += p16;", "if (rowsum == 1) l += p[key];"),
+    ("weights reading: FP16 term unrounded", "if (rowsum >= 1) l += p16;", "if (rowsum >= 1) l += p[key];"),
     ("weights reading: FP4 group scale dropped", "l += e8m0_value(ps) * gw;", "l += gw;"),
     ("max-pooled score misses the last key row",
      "for (int r = 0; r < 64; r++) {\n    double s = 0.0;\n    for (int c = 0; c < d; c++) s += (double)q[c]",
