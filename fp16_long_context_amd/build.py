@@ -17,6 +17,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libthrift.so")
 SOURCES = ["api.hip", "quantize.hip", "select.hip", "attn_fwd.hip"]
+# a standalone measurement program (issue costs of the FP4 step's
+# instructions), not part of the library
+ISA_COSTS = os.path.join(HERE, "isa_costs")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
@@ -55,8 +58,19 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    def compile_isa_costs() -> None:
+        tmp = ISA_COSTS + ".tmp"
+        r = subprocess.run([hipcc, *FLAGS, *PER_FILE["attn_fwd.hip"], os.path.join(CSRC, "isa_costs.hip"), "-o", tmp],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            err = "\n".join(x for x in r.stderr.splitlines() if "packed-fp32-ops" not in x)
+            raise RuntimeError(f"hipcc failed for isa_costs.hip:\n{err}")
+        os.replace(tmp, ISA_COSTS)
+
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        side = ex.submit(compile_isa_costs)
         objs = list(ex.map(compile_one, SOURCES))
+        side.result()
     tmp = SO + ".tmp"
     subprocess.run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], check=True)
     os.replace(tmp, SO)
