@@ -26,9 +26,11 @@ __device__ __forceinline__ int mx_scale_byte(float amax) {
   return s > 0 ? s : 0;
 }
 
-// The power of two the hardware convert divides by for scale byte s (s >= 1);
-// byte 0 only occurs for groups whose values are all zero or below 2^-124,
-// which convert to zero codes under a divisor of 1.
+// The power of two the hardware convert divides by for scale byte s (s >= 1).
+// Byte 0 (2^-127, an fp32 subnormal) only occurs for groups whose values
+// are all zero or below 2^-124: they take a divisor of 1 and so all-zero
+// codes, where the MX rule would keep codes for values from 2^-129 up (the
+// one documented departure from the rule; only re-quantized P reaches it).
 __device__ __forceinline__ float mx_scale_divisor(int s) { return s > 0 ? __uint_as_float((uint32_t)s << 23) : 1.0f; }
 
 // Two fp32 values divided by `div` and rounded to E2M1 (nearest-even,

@@ -36,7 +36,13 @@
  *     2j of a group in the low nibble of byte j) with one E8M0 scale byte per
  *     32 elements; scale exponent = floor(log2 amax) - 2 (byte 0 for an
  *     all-zero group), elements rounded to nearest-even on the E2M1 grid and
- *     saturated to +-6.
+ *     saturated to +-6.  One exception, inside thrift_attn_fwd only: a group
+ *     of re-quantized P whose largest weight is below 2^-124 (scale byte 0)
+ *     gets all-zero codes, where the rule would keep codes for its weights
+ *     from 2^-129 up.  Such a group's weights are below 2^-119 of the row's
+ *     largest, far under the output tolerance; Q, K and V groups (fp16 or
+ *     bf16 values, |x| >= 2^-24 when non-zero) never reach byte 0 unless
+ *     they are all zero.
  */
 #ifndef THRIFT_H
 #define THRIFT_H
@@ -96,7 +102,8 @@ int thrift_quantize(const thrift_shape *s, int in_dtype, const void *q, const vo
                     void *v4s, void *stream);
 
 /* Bytes of device workspace thrift_select needs (pooled fp32 means of Q and
- * K): 4 * nb * d * B * (Hq + Hkv).  Returns 0 for an invalid shape. */
+ * K): 4 * nb * d * B * (Hq + Hkv), e.g. 40 MiB for B = 1, Hq = 32, Hkv = 8,
+ * N = 131072, d = 128.  Returns 0 for an invalid shape. */
 size_t thrift_select_workspace_bytes(const thrift_shape *s);
 
 /* int32 entries of the traversal-list array: B * Hq * nb(nb+1)/2 (causal) or
@@ -247,7 +254,8 @@ int thrift_attn_fwd_ex(const thrift_shape *s, float sm_scale, const void *q16, c
                        void *const *events);
 
 /* Bytes of device workspace thrift_attn_fwd (and thrift_attn_fwd_wsum) needs
- * for shape s (0 if s is invalid): B * Hq * N/64 * (2 * 64 * (d/2 + 2) + 1) * 4. */
+ * for shape s (0 if s is invalid): B * Hq * N/64 * (2 * 64 * (d/2 + 2) + 1) * 4,
+ * e.g. 2214854656 bytes (2.06 GiB) for B = 1, Hq = 32, N = 131072, d = 128. */
 size_t thrift_attn_workspace_bytes(const thrift_shape *s);
 
 /* Static string naming a status code. */

@@ -155,6 +155,18 @@ def test_workspace(L):
     assert attn(L, s, ws=ctypes.c_void_p(0x10004), wsb=need_a) == EINVAL
 
 
+def test_documented_sizes_at_the_long_context_shape(L):
+    # the figures include/thrift.h quotes for B=1, Hq=32, Hkv=8, N=131072, d=128
+    s = shape(B=1, Hq=32, Hkv=8, N=131072, d=128)
+    nb = 131072 // 64
+    assert L.thrift_attn_workspace_bytes(ctypes.byref(s)) == 32 * nb * (2 * 64 * (128 // 2 + 2) + 1) * 4
+    assert L.thrift_attn_workspace_bytes(ctypes.byref(s)) == 2214854656  # 2.06 GiB
+    assert L.thrift_select_workspace_bytes(ctypes.byref(s)) == 4 * nb * 128 * (32 + 8) == 40 << 20
+    assert L.thrift_list_entries(ctypes.byref(s)) == 32 * nb * (nb + 1) // 2
+    hdr = open(os.path.join(ROOT, "include", "thrift.h")).read()
+    assert "2214854656 bytes (2.06 GiB)" in hdr and "40 MiB" in hdr
+
+
 def test_largest_grid_is_accepted(L):
     s = shape(B=2047, Hq=1024, Hkv=1024, N=512)  # 2^24 - 8192 query-block workgroups
     assert L.thrift_list_entries(ctypes.byref(s)) == 2047 * 1024 * 8 * 9 // 2

@@ -155,22 +155,39 @@ def test_output_dtypes_and_determinism():
     assert torch.equal(o2, o32)
 
 
-def sample_rows(x, B, Hq, N, n, seed):
+def sample_rows(x, B, Hq, N, n, seed, heads=(), batches=None):
+    """Rows to compare at full size: n random rows, the last row of the first
+    and last head of every batch, rows that look up a planted needle, and
+    for each (b, h) in batches x heads one row of every query block, at a
+    position that moves through the block and alternates between its two
+    32-row halves (the two waves of the FP4 workgroup)."""
     g = np.random.default_rng(seed)
     rows = list(g.integers(0, B * Hq * N, n))
     rows += [(b * Hq + h) * N + N - 1 for b in range(B) for h in (0, Hq - 1)]  # longest rows
     for (b, kvh, hq, p, t) in x["needles"][:8]:  # rows that look up a planted needle
         rows.append((b * Hq + hq) * N + t)
+    nb = N // 64
+    for b in (range(B) if batches is None else batches):
+        for h in heads:
+            i = np.arange(nb)
+            t = 64 * i + 32 * (i % 2) + (i * 7 + h * 13 + b * 5) % 32
+            rows += list((b * Hq + h) * N + t)
     return np.array(sorted(set(int(r) for r in rows)), dtype=np.int64)
+
+
+# per workload: query heads with one row of every query block (heads 0 and 1
+# share a two-head FP4 workgroup; the last head is in the last KV group)
+FULL_SIZE_HEADS = {"llama8b_16k": tuple(range(32)), "batched_32k": (0, 1, 27), "long_128k": (0, 1, 31)}
 
 
 @pytest.mark.parametrize("name", ["llama8b_16k", "batched_32k", "long_128k"])
 def test_full_size_workloads_sampled(name):
     # full sizes, the launch configuration the benchmark times; attention
-    # checked on sampled rows (every list and code is checked in full)
+    # checked on several thousand rows (every list and code is checked in full)
     x = synth.generate(name)
     w = x["w"]
-    rows = sample_rows(x, w.B, w.Hq, w.N, 40, 7)
+    rows = sample_rows(x, w.B, w.Hq, w.N, 40, 7, heads=FULL_SIZE_HEADS[name])
+    say(f"[case] {name}: {len(rows)} rows compared")
     run_case(x["q"], x["k"], x["v"], w.frac, rows=rows, label=name)
 
 
@@ -188,7 +205,8 @@ def test_frac_sweep_64k_sampled():
     for n in g:
         assert np.array_equal(g[n], qz_o[n]), f"sweep_64k: {n} differs"
     del g
-    rows = sample_rows(x, w.B, w.Hq, w.N, 24, 11)
+    rows = sample_rows(x, w.B, w.Hq, w.N, 24, 11, heads=(0, w.Hq - 1))
+    say(f"[case] sweep_64k: {len(rows)} rows compared at every fraction")
     for frac in (0.0, 0.01, 0.05, 0.2, 1.0):
         sel_o = oracle.select(qz_o["q16"], qz_o["k16"], frac, True)
         idx, n16 = binding.select(qz["q16"], qz["k16"], frac, True)

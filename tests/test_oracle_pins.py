@@ -413,6 +413,57 @@ def test_frac0_within_p_quantization_bound_of_dequantized_attention(orc):
     assert diff.max() > 1e-4  # and P quantization really is in effect
 
 
+def np_e2m1(mag):
+    """Nearest E2M1 magnitude of each value of `mag` (>= 0, already divided by
+    the group scale), ties to the even code, saturating at 6."""
+    dist = np.abs(mag[..., None] - E2M1)
+    tie_rank = np.where(dist == dist.min(-1, keepdims=True), np.arange(8) % 2, 9)  # even code first
+    return E2M1[tie_rank.argmin(-1)]
+
+
+def np_mx_groups(x):
+    """MXFP4 quantize-dequantize of the last axis in aligned groups of 32:
+    scale 2^e with e = floor(log2 amax) - 2 (from frexp, exact), clamped to
+    [-127, 127]; an all-zero group keeps zeros."""
+    g = x.reshape(*x.shape[:-1], -1, 32)
+    amax = np.abs(g).max(-1)
+    _, E = np.frexp(amax)  # amax = m 2^E, 0.5 <= m < 1: floor(log2 amax) = E - 1
+    e = np.clip(np.where(amax > 0, E - 3, -127), -127, 127)
+    scale = np.ldexp(1.0, e)[..., None]
+    return (np.sign(g) * np_e2m1(np.abs(g) / scale) * scale).reshape(x.shape)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,N,seed", [(64, 2, 1, 512, 41), (128, 2, 2, 256, 43)])
+def test_frac0_equals_numpy_one_shot_pure_fp4(orc, d, Hq, Hkv, N, seed):
+    # fraction 0 is pure-FP4 attention: an independent numpy computation of
+    # it, from its own MXFP4 quantizer on (fp16-exact inputs), in one shot per
+    # row: scores of the dequantized Q4, K4 times c = fl32(fl32(1/sqrt d)
+    # log2 e), one integer M = ceil(max) per row, p = fl32(2^(x - M)), P
+    # quantized in aligned 32-key groups (masked keys as zeros), output
+    # (P4 V4) / sum p
+    q, k, v = synth.random_qkv(1, Hq, Hkv, N, d, "fp16", seed=seed)
+    qz, sel, res = run_oracle(orc, q, k, v, "fp16", 0.0)
+    qn, kn, vn = (t.double().numpy()[0] for t in (q, k, v))
+    q4, k4 = np_mx_groups(qn), np_mx_groups(kn)
+    v4 = np_mx_groups(np.swapaxes(vn, -1, -2))  # along tokens: [Hkv, d, N]
+    sc = lambda s: 2.0 ** (s.astype(float) - 127)  # noqa: E731
+    # the two quantizers agree (values; the sign of a zero is not compared)
+    assert np.array_equal(q4, deq_codes(unpack(qz["q4"]))[0] * np.repeat(sc(qz["q4s"][0]), 32, -1))
+    assert np.array_equal(k4, deq_codes(unpack(qz["k4"]))[0] * np.repeat(sc(qz["k4s"][0]), 32, -1))
+    assert np.array_equal(v4, deq_codes(unpack(qz["v4"]))[0] * np.repeat(sc(qz["v4s"][0]), 32, -1))
+    c = float(np.float32(float(np.float32(1.0 / np.sqrt(d))) * 1.4426950408889634074))
+    causal = np.tril(np.ones((N, N), bool))
+    want = np.empty((Hq, N, d))
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        x = np.where(causal, (q4[h] @ k4[g].T) * c, -np.inf)
+        M = np.ceil(x.max(1, keepdims=True))
+        p = np.exp2(x - M).astype(np.float32).astype(np.float64)
+        want[h] = (np_mx_groups(p) @ v4[g].T) / p.sum(1, keepdims=True)
+    got = res["out"].reshape(Hq, N, d)
+    assert np.abs(got - want).max() <= 1e-12 * np.abs(want).max()
+
+
 # ------------------------------------------- row sum over the quantized weights
 # The alternative reading of the row sum: l adds the weights the P.V products
 # use (fp16(p) on FP16 tiles, the dequantized MXFP4 P on FP4 tiles).
