@@ -44,7 +44,7 @@ const char *thrift_status_str(int status) {
 
 size_t thrift_select_workspace_bytes(const thrift_shape *s) {
   if (check_shape(s) != THRIFT_OK) return 0;
-  return (size_t)4 * (size_t)(s->N / 64) * (size_t)s->d * (size_t)s->B * (size_t)(s->Hq + s->Hkv);
+  return sizeof(float) * select_workspace_floats(s->B, s->Hq, s->Hkv, s->N, s->d);
 }
 
 int64_t thrift_list_entries(const thrift_shape *s) {
@@ -86,9 +86,8 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
   SelectArgs a;
   a.q16 = (const uint16_t *)q16; a.k16 = (const uint16_t *)k16;
   a.idx = idx; a.n16 = n16;
-  a.qbar = (float *)workspace;
-  a.kbarT = (float *)workspace + (size_t)s->B * s->Hq * (s->N / 64) * s->d;
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
+  select_layout(a, (float *)workspace);
   a.ppm = (int64_t)llround(frac * 1e6);
   return launch_select(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
 }
@@ -107,9 +106,8 @@ static int select_args(const thrift_shape *s, double frac, int score, const void
   if (!aligned_ok(workspace)) return THRIFT_EINVAL;
   a.q16 = (const uint16_t *)q16; a.k16 = (const uint16_t *)k16;
   a.idx = idx; a.n16 = n16;
-  a.qbar = (float *)workspace;
-  a.kbarT = (float *)workspace + (size_t)s->B * s->Hq * (s->N / 64) * s->d;
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
+  select_layout(a, (float *)workspace);
   a.ppm = (int64_t)llround(frac * 1e6);
   a.kind = score;
   return THRIFT_OK;
@@ -145,7 +143,7 @@ int thrift_select_noalloc(const thrift_shape *s, double frac, const void *q16, c
   SelectArgs a;
   a.q16 = (const uint16_t *)q16; a.k16 = (const uint16_t *)k16;
   a.idx = idx; a.n16 = n16;
-  a.qbar = nullptr; a.kbarT = nullptr;  // set by the launcher
+  a.qbar = a.kbarT = a.qn = a.kn = a.knmax = nullptr;  // set by the launcher
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
   a.ppm = (int64_t)llround(frac * 1e6);
   return launch_select_scratch(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;

@@ -165,6 +165,170 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(SelectArgs a, int 
   }
 }
 
+// Tile (ti, tj) of head-tile index t (causal heads: the tiles on and below the diagonal,
+// row-major; else tn x tn).
+__device__ __forceinline__ void tile_of(const int t, const int causal, const int tn, int &ti, int &tj) {
+  if (causal) {
+    ti = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ti++;
+    while (ti * (ti + 1) / 2 > t) ti--;
+    tj = t - ti * (ti + 1) / 2;
+  } else {
+    ti = t / tn;
+    tj = t % tn;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The selection's own scoring of pooled means, in fp32.  The selection
+// needs the order of the fp64 chains, not their values: a sequential fp32
+// fma chain over d channels differs from the exact dot product by at most
+// gamma_d sum_c |q_c k_c| <= gamma_d |q| |k| (gamma_d = d u / (1 - d u),
+// u = 2^-24; Cauchy-Schwarz), and the fp64 chain from it by far less, so
+// every fp32 score lies within M = 2 d 2^-24 |q_i| max_j |k_j| of the fp64
+// score (the factor 2 covers gamma_d's own correction, the fp64 chain's
+// error and the norms' roundings, all below 2^-40 relative).  The select
+// kernel takes every block whose fp32 score clears the fp32 cut-off by more
+// than 2M, drops every block below it by more than 2M, and decides the rest
+// by their fp64 chains: the same lists as ranking every fp64 score.
+
+// Euclidean norms of the Q means ([BH, nb], row-major source): fp64 sum of
+// the exact squares, fp64 sqrt, rounded up to fp32.  One thread per row.
+template <int D>
+__global__ __launch_bounds__(256) void qnorm_kernel(const float *__restrict__ qbar, float *__restrict__ qn,
+                                                    const int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const float4 *q = (const float4 *)(qbar + r * D);
+  double ss = 0.0;
+#pragma unroll 8
+  for (int c = 0; c < D / 4; c++) {
+    const float4 v = q[c];
+    ss = fma((double)v.x, (double)v.x, ss);
+    ss = fma((double)v.y, (double)v.y, ss);
+    ss = fma((double)v.z, (double)v.z, ss);
+    ss = fma((double)v.w, (double)v.w, ss);
+  }
+  qn[r] = __double2float_ru(sqrt(ss));
+}
+
+// Norms of the K means ([BHkv, d, nb], channel-major source) and, per KV
+// head, their largest over blocks 1 .. nb-1 (block 0 is always on the FP16
+// list, never a candidate).  One workgroup per KV head; thread t takes
+// blocks t, t + 256, ...
+template <int D>
+__global__ __launch_bounds__(256) void knorm_kernel(const float *__restrict__ kbarT, float *__restrict__ kn,
+                                                    float *__restrict__ knmax, const int nb) {
+  __shared__ float part[4];
+  const int64_t hk = blockIdx.x;
+  const float *kb = kbarT + hk * D * (int64_t)nb;
+  float mx = 0.0f;
+  for (int j = threadIdx.x; j < nb; j += 256) {
+    double ss = 0.0;
+#pragma unroll 8
+    for (int c = 0; c < D; c++) {
+      const double v = (double)kb[(int64_t)c * nb + j];
+      ss = fma(v, v, ss);
+    }
+    const float n = __double2float_ru(sqrt(ss));
+    kn[hk * nb + j] = n;
+    if (j > 0) mx = fmaxf(mx, n);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) knmax[hk] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
+// fp32 pooled-mean scores: every causal score of a 128 x 128 tile of (query
+// block, key block) pairs per workgroup of 256 threads, written as fp32 bits
+// at the list positions.  Thread (tr, tc) = (t / 16, t % 16) owns query
+// blocks 4 tr + {0..3, 64..67} and key blocks 4 tc + {0..3, 64..67}, so each
+// channel step reads 4 x 16 bytes of LDS (consecutive lanes, consecutive
+// 16-byte chunks) for 64 fmas; the means are staged 32 channels at a time,
+// channel-major, and each chain runs over the channels in order.
+constexpr int kS32Tile = 128, kS32Chunk = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void score32_kernel(SelectArgs a, int tiles_per_head, int tn) {
+  __shared__ __attribute__((aligned(16))) float qs[kS32Chunk][kS32Tile];
+  __shared__ __attribute__((aligned(16))) float ks[kS32Chunk][kS32Tile];
+  const int nb = a.N / 64;
+  const int64_t bh = blockIdx.x / tiles_per_head;
+  int ti, tj;
+  tile_of(blockIdx.x % tiles_per_head, a.causal, tn, ti, tj);
+  const int i0 = kS32Tile * ti, j0 = kS32Tile * tj;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int g = (int)((int64_t)h * a.Hkv / a.Hq);
+  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const float *qb = a.qbar + (bh * nb + i0) * (int64_t)D;
+  const float *kb = a.kbarT + ((int64_t)b * a.Hkv + g) * D * (int64_t)nb + j0;
+  float s[8][8];
+#pragma unroll
+  for (int u = 0; u < 8; u++)
+#pragma unroll
+    for (int v = 0; v < 8; v++) s[u][v] = 0.0f;
+  for (int c0 = 0; c0 < D; c0 += kS32Chunk) {
+    // staging loads, all issued before any is used: Q rows (8 float4 per
+    // 32-channel row segment), K channel rows (scalar: nb need not be a
+    // multiple of 4); rows and blocks past nb read in bounds and become 0
+    float4 qv[4];
+    float kv[16];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = tid + 256 * u, r = e >> 3, q4 = e & 7;
+      qv[u] = *(const float4 *)(qb + (int64_t)min(r, nb - 1 - i0) * D + c0 + 4 * q4);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; u++) {
+      const int e = tid + 256 * u, c = e >> 7, j = e & 127;
+      kv[u] = kb[(int64_t)(c0 + c) * nb + min(j, nb - 1 - j0)];
+    }
+    if (c0 > 0) __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = tid + 256 * u, r = e >> 3, q4 = e & 7;
+      const bool ok = i0 + r < nb;
+      qs[4 * q4 + 0][r] = ok ? qv[u].x : 0.0f;
+      qs[4 * q4 + 1][r] = ok ? qv[u].y : 0.0f;
+      qs[4 * q4 + 2][r] = ok ? qv[u].z : 0.0f;
+      qs[4 * q4 + 3][r] = ok ? qv[u].w : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; u++) {
+      const int e = tid + 256 * u, c = e >> 7, j = e & 127;
+      ks[c][j] = (j0 + j < nb) ? kv[u] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = 0; c < kS32Chunk; c++) {
+      const float4 qa = *(const float4 *)&qs[c][4 * tr], qb4 = *(const float4 *)&qs[c][64 + 4 * tr];
+      const float4 ka = *(const float4 *)&ks[c][4 * tc], kb4 = *(const float4 *)&ks[c][64 + 4 * tc];
+      const float qd[8] = {qa.x, qa.y, qa.z, qa.w, qb4.x, qb4.y, qb4.z, qb4.w};
+      const float kd[8] = {ka.x, ka.y, ka.z, ka.w, kb4.x, kb4.y, kb4.z, kb4.w};
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+#pragma unroll
+        for (int v = 0; v < 8; v++) s[u][v] = fmaf(qd[u], kd[v], s[u][v]);
+    }
+  }
+  const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
+  int32_t *base = a.idx + bh * per;
+#pragma unroll
+  for (int u = 0; u < 8; u++) {
+    const int i = i0 + 4 * tr + (u & 3) + 64 * (u >> 2);
+    if (i >= nb) continue;
+    const int nv = a.causal ? i + 1 : nb;
+    int32_t *row = base + row_offset(i, nb, a.causal);
+#pragma unroll
+    for (int v = 0; v < 8; v++) {
+      const int j = j0 + 4 * tc + (v & 3) + 64 * (v >> 2);
+      if (j < nv) row[j] = __float_as_int(s[u][v]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Other block scores (the heuristic is the method's open risk: the
 // hotpaper.ai summary of the ThriftAttention paper, section on significance
@@ -216,18 +380,6 @@ __global__ __launch_bounds__(128) void normw_pool_kernel(const uint16_t *__restr
   }
 }
 
-// Tile (ti, tj) of head-tile index t (as score_kernel).
-__device__ __forceinline__ void tile_of(const int t, const int causal, const int tn, int &ti, int &tj) {
-  if (causal) {
-    ti = (int)((sqrt(8.0 * t + 1.0) - 1.0) * 0.5);
-    while ((ti + 1) * (ti + 2) / 2 <= t) ti++;
-    while (ti * (ti + 1) / 2 > t) ti--;
-    tj = t - ti * (ti + 1) / 2;
-  } else {
-    ti = t / tn;
-    tj = t % tn;
-  }
-}
 
 // Max-pooled scores: the 64 x 64 block-pair tile of score_kernel, with the
 // key side one row r of every key block at a time: the query means stay in
@@ -392,6 +544,10 @@ __device__ __forceinline__ uint64_t order_key64(double s) {
   const uint64_t u = __double_as_longlong(s);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
+// The fp32 value of a nonzero order key.
+__device__ __forceinline__ float key32_value(const uint32_t k) {
+  return __uint_as_float((k >> 31) ? (k & 0x7fffffffu) : ~k);
+}
 
 // Number of the wave's keys (KPL per lane) at or above c.
 template <int KPL>
@@ -457,9 +613,11 @@ __device__ __forceinline__ double exact_score(const float *qrow, const float *kT
 // The fp64 block score of kind `kind` for key block j of a query row: the
 // pooled or norm-weighted means' chain (qrow, kT), the max over the key rows
 // of (qrow . k_r), or the max over every row pair of the two blocks.
+// (A call, not inlined: the selection reaches it only for the few blocks
+// near its cut-off, from several unrolled sites.)
 template <int D>
-__device__ double exact_score_kind(const int kind, const float *qrow, const float *kT, const int nb,
-                                   const uint16_t *qblk, const uint16_t *kh, const int j) {
+__device__ __noinline__ double exact_score_kind(const int kind, const float *qrow, const float *kT, const int nb,
+                                                const uint16_t *qblk, const uint16_t *kh, const int j) {
   if (kind == kScoreMaxPooled || kind == kScoreBlockMax) {
     const uint16_t *kblk = kh + (int64_t)64 * j * D;
     double best = -INFINITY;
@@ -478,20 +636,37 @@ __device__ double exact_score_kind(const int kind, const float *qrow, const floa
   return exact_score<D>(qrow, kT, nb, j);
 }
 
+// Undecided blocks of a row (those in the band around the cut-off) are
+// ranked through LDS when there are at most kBand of them: per wave kBand
+// 64-bit exact keys, kBand block indices and one decision byte per block.
+constexpr int kBand = 64;
+__host__ __device__ constexpr size_t select_lds_per_wave(const int nb) {
+  return (size_t)kBand * (8 + 4) + (((size_t)nb + 15) & ~(size_t)15);
+}
+
 // KPL: keys per lane, at least ceil(nb / 64).  Lane l holds blocks l + 64 t.
-// LDS: nb 64-bit keys per wave for the blocks tied at the fp32 cut-off.
+// The scores in the list array are fp32: the rounded fp64 scores of a.kind
+// (margin 0: only blocks equal to the cut-off are undecided), or, for
+// pooled means, the fp32 chains of score32_kernel (margin M: the blocks
+// within 2M of the cut-off are undecided).  Undecided blocks are ranked by
+// their fp64 scores, the lower block index first among equal ones.
 template <int D, int KPL>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a, int waves_per_wg) {
-  extern __shared__ uint64_t tie64[];
+__global__ __launch_bounds__(kSelThreads)
+__attribute__((amdgpu_waves_per_eu(KPL <= 16 ? 4 : (KPL <= 32 ? 3 : 1)))) void select_kernel(SelectArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sel_lds[];
   const int nb = a.N / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * waves_per_wg + wave;  // = (b*Hq + h)*nb + i
-  if (wave >= waves_per_wg || row >= (int64_t)a.B * a.Hq * nb) return;
+  const int64_t row = (int64_t)blockIdx.x * (kSelThreads / 64) + wave;  // = (b*Hq + h)*nb + i
+  if (row >= (int64_t)a.B * a.Hq * nb) return;
   const int i = (int)(row % nb);
   const int64_t bh = row / nb;
   const int nv = a.causal ? i + 1 : nb;
   const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
   int32_t *out = a.idx + bh * per + row_offset(i, nb, a.causal);
+  uint8_t *wl = sel_lds + (size_t)wave * select_lds_per_wave(nb);
+  uint64_t *band_key = (uint64_t *)wl;
+  int32_t *band_blk = (int32_t *)(wl + kBand * 8);
+  uint8_t *decided = wl + kBand * 12;
 
   if (a.ppm == 0) {  // no FP16 blocks: the FP4 list is every valid block
     for (int j = lane; j < nv; j += 64) out[j] = j;
@@ -505,15 +680,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a, int w
   const int kextra = (int)kk - nforced;  // best non-forced blocks to add
   const bool scored = kextra > 0 && kextra < nv - nforced;
 
-  // key: order key of the block's fp32 score (0: not a candidate); blocks
-  // above the cut-off T are taken, those tied with it are decided below
+  // key: order key of the block's fp32 score (0: not a candidate).  Blocks
+  // above the band [Tlo, Thi] around the cut-off are taken; `take` of the
+  // band's `nband` blocks join them: all of them (mode 0), those marked in
+  // `decided` (mode 1, at most kBand in the band), or by the T64 rule (mode
+  // 2, a wider band).
   uint32_t key[KPL];
-  uint32_t T = 0;
-  int take_eq = 0;       // how many blocks tied at T join the FP16 list
-  bool exact = false;    // the tied blocks need their fp64 scores
+  uint32_t Tlo = 0, Thi = 0;
+  int mode = 0;
   uint64_t T64 = 0;
   int take_eq64 = 0;
-  uint64_t *tk = tie64 + (size_t)wave * nb;
+  const float *qrow = nullptr, *kT = nullptr;
+  const uint16_t *kh = nullptr, *qblk = nullptr;
   if (scored) {
     // every load is issued before any is used (an out-of-row lane reads
     // entry 0 and discards it)
@@ -529,68 +707,111 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a, int w
       const uint32_t k32 = order_key32_bits((uint32_t)raw[t]);
       key[t] = (j < nv && j != 0 && j != i) ? k32 : 0u;
     }
-    T = kth_largest<KPL>(key, kextra);
-    int gt = 0, eq = 0;
+    const uint32_t T = kth_largest<KPL>(key, kextra);
+    Tlo = Thi = T;
+    const int g = (int)((int64_t)(bh % a.Hq) * a.Hkv / a.Hq), b = (int)(bh / a.Hq);
+    if (a.kind == kScorePooled) {
+      // fp32 chains: the band is the cut-off +- 2M, rounded outwards
+      const double M = 2.0 * D * 0x1p-24 * (double)a.qn[row] * (double)a.knmax[(int64_t)b * a.Hkv + g];
+      const double c = (double)key32_value(T);
+      Thi = order_key32_bits(__float_as_uint(__double2float_ru(c + 2.0 * M)));
+      Tlo = max(order_key32_bits(__float_as_uint(__double2float_rd(c - 2.0 * M))), 1u);
+    }
+    int gt = 0, nband = 0;
 #pragma unroll
     for (int t = 0; t < KPL; t++) {
-      gt += __popcll(__ballot(key[t] > T));
-      eq += __popcll(__ballot(key[t] == T));
+      gt += __popcll(__ballot(key[t] > Thi));
+      nband += __popcll(__ballot(key[t] >= Tlo && key[t] <= Thi));
     }
-    take_eq = kextra - gt;  // 1 .. eq
-    exact = take_eq < eq;
-    if (exact) {
-      // the fp64 scores of the tied blocks decide; among equal fp64 scores
-      // the lower block index wins
-      const int g = (int)((int64_t)(bh % a.Hq) * a.Hkv / a.Hq), b = (int)(bh / a.Hq);
-      const float *qrow = a.qbar + row * (int64_t)D;
-      const float *kT = a.kbarT + ((int64_t)b * a.Hkv + g) * D * (int64_t)nb;
-      const uint16_t *kh = a.k16 + ((int64_t)b * a.Hkv + g) * a.N * (int64_t)D;
-      const uint16_t *qblk = a.q16 + (bh * a.N + 64 * (int64_t)i) * D;
-      uint64_t mx = 0, mn = ~0ull;
+    const int take = kextra - gt;  // 1 .. nband
+    if (take < nband) {
+      // the fp64 scores of the band's blocks decide; among equal fp64
+      // scores the lower block index wins
+      qrow = a.qbar + row * (int64_t)D;
+      kT = a.kbarT + ((int64_t)b * a.Hkv + g) * D * (int64_t)nb;
+      kh = a.k16 + ((int64_t)b * a.Hkv + g) * a.N * (int64_t)D;
+      qblk = a.q16 + (bh * a.N + 64 * (int64_t)i) * D;
+      const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      if (nband <= kBand) {
+        mode = 1;
+        // the band's blocks, ascending, one per lane; their exact keys; each
+        // lane counts the band blocks ranked before its own
+        int base = 0;
 #pragma unroll
-      for (int t = 0; t < KPL; t++) {
-        const int j = lane + 64 * t;
-        uint64_t k64 = 0;
-        if (key[t] == T) k64 = order_key64(exact_score_kind<D>(a.kind, qrow, kT, nb, qblk, kh, j));
-        if (j < nb) tk[j] = k64;
-        mx = k64 > mx ? k64 : mx;
-        mn = (k64 && k64 < mn) ? k64 : mn;
-      }
-      // this wave reads back what its other lanes wrote (LDS is in order
-      // for one wave; the barrier keeps the compiler from reordering)
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint64_t ox = __shfl_xor(mx, off, 64), on = __shfl_xor(mn, off, 64);
-        mx = ox > mx ? ox : mx;
-        mn = on < mn ? on : mn;
-      }
-      // take_eq-th largest 64-bit key among the tied blocks (bitwise search
-      // below the bits common to all of them)
-      const uint64_t diff = mx ^ mn;
-      uint64_t t64 = mx;
-      if (diff) {
-        const int top = 63 - __builtin_clzll(diff);
-        t64 = mx & ~((top == 63) ? ~0ull : ((2ull << top) - 1ull));
-        for (int bit = top; bit >= 0; bit--) {
-          const uint64_t c = t64 | (1ull << bit);
-          int n = 0;
-#pragma unroll
-          for (int t = 0; t < KPL; t++) {
-            const int j = lane + 64 * t;
-            n += __popcll(__ballot(j < nb && tk[j] >= c));
-          }
-          if (n >= take_eq) t64 = c;
+        for (int t = 0; t < KPL; t++) {
+          const bool in = key[t] >= Tlo && key[t] <= Thi;
+          const uint64_t bal = __ballot(in);
+          if (in) band_blk[base + __popcll(bal & lower)] = lane + 64 * t;
+          base += __popcll(bal);
         }
-      }
-      int gt64 = 0;
+        // LDS is in order for one wave; the barrier keeps the compiler from
+        // reordering the reads above the writes
+        __builtin_amdgcn_wave_barrier();
+        int myj = 0;
+        uint64_t myk = 0;
+        if (lane < nband) {
+          myj = band_blk[lane];
+          myk = order_key64(exact_score_kind<D>(a.kind, qrow, kT, nb, qblk, kh, myj));
+          band_key[lane] = myk;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane < nband) {
+          int rank = 0;
+          for (int m = 0; m < nband; m++) {
+            const uint64_t km = band_key[m];
+            rank += (km > myk || (km == myk && band_blk[m] < myj)) ? 1 : 0;
+          }
+          decided[myj] = rank < take ? 1 : 0;
+        }
+        __builtin_amdgcn_wave_barrier();
+      } else {
+        mode = 2;
+        // a wide band: the take-th largest exact key T64 by a bitwise search
+        // below the bits its keys share (exact scores recomputed per pass)
+        uint64_t mx = 0, mn = ~0ull;
 #pragma unroll
-      for (int t = 0; t < KPL; t++) {
-        const int j = lane + 64 * t;
-        gt64 += __popcll(__ballot(j < nb && tk[j] > t64));
+        for (int t = 0; t < KPL; t++) {
+          if (key[t] >= Tlo && key[t] <= Thi) {
+            const uint64_t k64 = order_key64(exact_score_kind<D>(a.kind, qrow, kT, nb, qblk, kh, lane + 64 * t));
+            mx = k64 > mx ? k64 : mx;
+            mn = k64 < mn ? k64 : mn;
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const uint64_t ox = __shfl_xor(mx, off, 64), on = __shfl_xor(mn, off, 64);
+          mx = ox > mx ? ox : mx;
+          mn = on < mn ? on : mn;
+        }
+        const uint64_t diff = mx ^ mn;
+        uint64_t t64 = mx;
+        if (diff) {
+          const int top = 63 - __builtin_clzll(diff);
+          t64 = mx & ~((top == 63) ? ~0ull : ((2ull << top) - 1ull));
+          for (int bit = top; bit >= 0; bit--) {
+            const uint64_t c = t64 | (1ull << bit);
+            int n = 0;
+#pragma unroll
+            for (int t = 0; t < KPL; t++) {
+              const bool in = key[t] >= Tlo && key[t] <= Thi;
+              uint64_t k64 = 0;
+              if (in) k64 = order_key64(exact_score_kind<D>(a.kind, qrow, kT, nb, qblk, kh, lane + 64 * t));
+              n += __popcll(__ballot(in && k64 >= c));
+            }
+            if (n >= take) t64 = c;
+          }
+        }
+        int gt64 = 0;
+#pragma unroll
+        for (int t = 0; t < KPL; t++) {
+          const bool in = key[t] >= Tlo && key[t] <= Thi;
+          uint64_t k64 = 0;
+          if (in) k64 = order_key64(exact_score_kind<D>(a.kind, qrow, kT, nb, qblk, kh, lane + 64 * t));
+          gt64 += __popcll(__ballot(in && k64 > t64));
+        }
+        T64 = t64;
+        take_eq64 = take - gt64;  // lowest-index blocks with key == T64
       }
-      T64 = t64;
-      take_eq64 = take_eq - gt64;  // lowest-index blocks with key == T64
     }
   }
 
@@ -609,16 +830,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a, int w
     if (!scored) {
       sel = forced || kextra > 0;  // kextra > 0 here means every valid block
     } else {
-      // a nonzero key is a valid, non-forced block; T is nonzero
-      const bool tied = key[t] == T;
-      sel = forced || key[t] > T;
-      if (!exact) {
-        sel = sel || tied;  // every tied block is taken
+      // a nonzero key is a valid, non-forced block; Tlo is nonzero
+      const bool band = key[t] >= Tlo && key[t] <= Thi;
+      sel = forced || key[t] > Thi;
+      if (mode == 0) {
+        sel = sel || band;  // the whole band is taken
+      } else if (mode == 1) {
+        if (band) sel = decided[j] != 0;
       } else {
-        // (exact is wave-uniform: the ballot below runs on the whole wave)
-        const uint64_t k64 = tied ? tk[j] : 0ull;
+        // (mode is wave-uniform: the ballot below runs on the whole wave)
+        uint64_t k64 = 0;
+        if (band) k64 = order_key64(exact_score_kind<D>(a.kind, qrow, kT, nb, qblk, kh, j));
         sel = sel || k64 > T64;
-        const bool tie64 = tied && k64 == T64;
+        const bool tie64 = band && k64 == T64;
         const uint64_t tb = __ballot(tie64);
         if (tie64) sel = eq_seen + __popcll(tb & lower) < take_eq64;
         eq_seen += __popcll(tb);
@@ -635,15 +859,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a, int w
 template <int D, int KPL>
 static hipError_t launch_select_kpl(const SelectArgs &a, hipStream_t st) {
   const int nb = a.N / 64;
-  int wpw = (int)(65536 / ((size_t)nb * 8));
-  wpw = wpw < 1 ? 1 : (wpw > kSelThreads / 64 ? kSelThreads / 64 : wpw);
-  const size_t lds = (size_t)wpw * nb * 8;
+  constexpr int waves = kSelThreads / 64;
+  const size_t lds = waves * select_lds_per_wave(nb);
   const void *fn = (const void *)select_kernel<D, KPL>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.B * a.Hq * nb;
-  const unsigned grid = (unsigned)((rows + wpw - 1) / wpw);
-  hipLaunchKernelGGL((select_kernel<D, KPL>), dim3(grid), dim3(64 * wpw), lds, st, a, wpw);
+  const unsigned grid = (unsigned)((rows + waves - 1) / waves);
+  hipLaunchKernelGGL((select_kernel<D, KPL>), dim3(grid), dim3(kSelThreads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -693,11 +916,32 @@ static hipError_t launch_scores_d(const SelectArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The selection's pooled-mean scores: the means, their norms, then the
+// fp32 chains (score32_kernel) into a.idx.
+template <int D>
+static hipError_t launch_scores32_d(const SelectArgs &a, hipStream_t st) {
+  const int nb = a.N / 64;
+  auto grid = [](int64_t work) {
+    int64_t b = (work + 255) / 256;
+    return (unsigned)(b > 256 * 64 ? 256 * 64 : b);
+  };
+  const int64_t BHq = (int64_t)a.B * a.Hq, BHk = (int64_t)a.B * a.Hkv;
+  hipLaunchKernelGGL(pool_kernel<false>, dim3(grid(BHq * nb * D)), dim3(256), 0, st, a.q16, a.qbar, BHq, a.N, D);
+  hipLaunchKernelGGL(pool_kernel<true>, dim3(grid(BHk * nb * D)), dim3(256), 0, st, a.k16, a.kbarT, BHk, a.N, D);
+  hipLaunchKernelGGL(qnorm_kernel<D>, dim3((unsigned)((BHq * nb + 255) / 256)), dim3(256), 0, st, a.qbar, a.qn,
+                     BHq * nb);
+  hipLaunchKernelGGL(knorm_kernel<D>, dim3((unsigned)BHk), dim3(256), 0, st, a.kbarT, a.kn, a.knmax, nb);
+  const int tn = (nb + kS32Tile - 1) / kS32Tile;
+  const int tiles = a.causal ? tn * (tn + 1) / 2 : tn * tn;
+  hipLaunchKernelGGL(score32_kernel<D>, dim3((unsigned)(BHq * tiles)), dim3(256), 0, st, a, tiles, tn);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_select_d(const SelectArgs &a, hipStream_t st) {
   const int nb = a.N / 64;
   if (a.ppm > 0) {
-    const hipError_t e = launch_scores_d<D>(a, st);
+    const hipError_t e = a.kind == kScorePooled ? launch_scores32_d<D>(a, st) : launch_scores_d<D>(a, st);
     if (e != hipSuccess) return e;
   }
   const int kpl = (nb + 63) / 64;
@@ -753,8 +997,7 @@ hipError_t launch_select_scratch(SelectArgs a, hipStream_t st) {
     }
     ptr = g_scratch_ptr[dev];
   }
-  a.qbar = (float *)ptr;
-  a.kbarT = (float *)ptr + (size_t)a.B * a.Hq * (a.N / 64) * a.d;
+  select_layout(a, (float *)ptr);
   return launch_select(a, st);
 }
 

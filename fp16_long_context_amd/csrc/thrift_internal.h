@@ -52,10 +52,30 @@ struct SelectArgs {
   int32_t *idx, *n16;
   float *qbar;   // [B,Hq,nb,d]
   float *kbarT;  // [B,Hkv,d,nb]
+  float *qn;     // [B,Hq,nb]  Euclidean norms of the Q means, rounded up
+  float *kn;     // [B,Hkv,nb] Euclidean norms of the K means, rounded up
+  float *knmax;  // [B,Hkv]    largest K-mean norm over blocks 1 .. nb-1
   int B, Hq, Hkv, N, d, causal;
   int64_t ppm;
   int kind = 0;  // block score: 0 pooled mean, 1 max-pooled, 2 norm-weighted, 3 block max
 };
+
+// Selection workspace, in floats: the pooled means of Q and K, then the
+// norms of both and the largest K norm of each KV head.
+inline size_t select_workspace_floats(int B, int Hq, int Hkv, int N, int d) {
+  const size_t nb = (size_t)(N / 64), bq = (size_t)B * Hq, bk = (size_t)B * Hkv;
+  return nb * (size_t)(d + 1) * (bq + bk) + bk;
+}
+
+// Points the workspace arrays of a (shape fields set) into base.
+inline void select_layout(SelectArgs &a, float *base) {
+  const size_t nb = (size_t)(a.N / 64), bq = (size_t)a.B * a.Hq, bk = (size_t)a.B * a.Hkv;
+  a.qbar = base;
+  a.kbarT = a.qbar + bq * nb * a.d;
+  a.qn = a.kbarT + bk * nb * a.d;
+  a.kn = a.qn + bq * nb;
+  a.knmax = a.kn + bk * nb;
+}
 
 struct AttnArgs {
   const uint16_t *q16, *k16, *v16;

@@ -101,9 +101,11 @@ int thrift_quantize(const thrift_shape *s, int in_dtype, const void *q, const vo
                     void *q16, void *k16, void *v16, void *q4, void *q4s, void *k4, void *k4s, void *v4,
                     void *v4s, void *stream);
 
-/* Bytes of device workspace thrift_select needs (pooled fp32 means of Q and
- * K): 4 * nb * d * B * (Hq + Hkv), e.g. 40 MiB for B = 1, Hq = 32, Hkv = 8,
- * N = 131072, d = 128.  Returns 0 for an invalid shape. */
+/* Bytes of device workspace thrift_select needs (the pooled fp32 means of Q
+ * and K, their norms, the largest K norm of each KV head):
+ * 4 * (nb * (d + 1) * B * (Hq + Hkv) + B * Hkv), e.g. 42270752 bytes
+ * (40.3 MiB) for B = 1, Hq = 32, Hkv = 8, N = 131072, d = 128.  Returns 0
+ * for an invalid shape. */
 size_t thrift_select_workspace_bytes(const thrift_shape *s);
 
 /* int32 entries of the traversal-list array: B * Hq * nb(nb+1)/2 (causal) or
@@ -124,14 +126,18 @@ int64_t thrift_list_entries(const thrift_shape *s);
  *   else:      budget k = min(n_valid, max(|F|, ceil(ppm * n_valid / 1e6)));
  *              FP16 list = F plus the k - |F| best other blocks by
  *              (score descending, block index ascending).
- * The FP4 list is every other valid block.
+ * The FP4 list is every other valid block.  (The library ranks by fp32
+ * chains of the same products and recomputes the fp64 chain of every block
+ * whose fp32 score lies within the fp32 chains' error bound of the cut-off:
+ * the lists are those of the fp64 ranking, bit for bit.)
  *
  * frac in [0, 1].  Outputs:
  *   idx [B,Hq, rows]: row i starts at i(i+1)/2 (causal) or i*nb and holds the
  *        FP16 list ascending followed by the FP4 list ascending;
  *   n16 [B,Hq,nb]: length of each FP16 list.
  * workspace: device buffer of at least thrift_select_workspace_bytes(s)
- * bytes (contents on return: the pooled means, Q first then K).
+ * bytes (contents on return: the pooled means, Q first then K, then their
+ * norms; with frac 0 nothing is written).
  * Errors: THRIFT_EINVAL (pointer, frac), THRIFT_EWORKSPACE.
  */
 int thrift_select(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx,
@@ -176,8 +182,8 @@ int thrift_block_scores(const thrift_shape *s, int score, const void *q16, const
  * the same lists, bit for bit, with no workspace argument.  The pooled means
  * go to a static device array inside the library (64 MiB per GPU, held
  * until the process ends); the call itself allocates nothing.  Limit:
- * thrift_select_workspace_bytes(s) = 4 * nb * d * B * (Hq + Hkv) must not
- * exceed 64 MiB (e.g. B = 1, Hq = 32, Hkv = 8, d = 128 up to N = 209664),
+ * thrift_select_workspace_bytes(s) must not exceed 64 MiB (e.g. B = 1,
+ * Hq = 32, Hkv = 8, d = 128 up to N = 208064),
  * else THRIFT_EWORKSPACE and nothing is launched.  Every call on one GPU
  * shares that array: calls that overlap in time on one GPU (other streams,
  * other threads) race and must be serialized by the caller.

@@ -142,7 +142,7 @@ def test_attn_ex_rejects_unknown_rowsum(L):
 def test_workspace(L):
     s = shape()
     need = L.thrift_select_workspace_bytes(ctypes.byref(s))
-    assert need == 4 * 16 * 128 * 1 * (4 + 2)
+    assert need == 4 * (16 * (128 + 1) * 1 * (4 + 2) + 1 * 2)  # means, norms, per-KV-head max norm
     assert sel(L, s, ws=None) == EWS
     assert sel(L, s, wsb=need - 1) == EWS
     assert sel(L, s, ws=ctypes.c_void_p(0x10004), wsb=need) == EINVAL
@@ -161,10 +161,10 @@ def test_documented_sizes_at_the_long_context_shape(L):
     nb = 131072 // 64
     assert L.thrift_attn_workspace_bytes(ctypes.byref(s)) == 32 * nb * (2 * 64 * (128 // 2 + 2) + 1) * 4
     assert L.thrift_attn_workspace_bytes(ctypes.byref(s)) == 2214854656  # 2.06 GiB
-    assert L.thrift_select_workspace_bytes(ctypes.byref(s)) == 4 * nb * 128 * (32 + 8) == 40 << 20
+    assert L.thrift_select_workspace_bytes(ctypes.byref(s)) == 4 * (nb * 129 * (32 + 8) + 8) == 42270752
     assert L.thrift_list_entries(ctypes.byref(s)) == 32 * nb * (nb + 1) // 2
     hdr = open(os.path.join(ROOT, "include", "thrift.h")).read()
-    assert "2214854656 bytes (2.06 GiB)" in hdr and "40 MiB" in hdr
+    assert "2214854656 bytes (2.06 GiB)" in hdr and "42270752 bytes" in hdr
 
 
 def test_largest_grid_is_accepted(L):
@@ -265,12 +265,15 @@ def test_binding_rejects_short_lists_and_outputs():
 
 
 def test_noalloc_select_size_limit(L):
-    # the pooled means (4 nb d B (Hq + Hkv) bytes) must fit the library's
-    # 64 MiB static array: the 128K Llama-shaped layer fits, 8 more query
-    # heads do not; beyond the limit nothing is launched
+    # the selection workspace (means and norms) must fit the library's 64 MiB
+    # static array: the Llama-shaped layer fits up to N = 208064 (the
+    # header's figure), not one block more, nor two sequences of 128K;
+    # beyond the limit nothing is launched
     assert L.thrift_select_noalloc(None, 0.05, *[FAKE] * 4, None) == EINVAL
     fits = shape(B=1, Hq=32, Hkv=8, N=131072, d=128)
     assert L.thrift_select_workspace_bytes(ctypes.byref(fits)) <= 64 << 20
+    assert L.thrift_select_workspace_bytes(ctypes.byref(shape(B=1, Hq=32, Hkv=8, N=208064, d=128))) <= 64 << 20
+    assert L.thrift_select_workspace_bytes(ctypes.byref(shape(B=1, Hq=32, Hkv=8, N=208128, d=128))) > 64 << 20
     too_big = shape(B=2, Hq=32, Hkv=8, N=131072, d=128)
     assert L.thrift_select_workspace_bytes(ctypes.byref(too_big)) > 64 << 20
     assert sel_noalloc(L, too_big) == EWS
