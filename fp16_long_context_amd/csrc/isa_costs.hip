@@ -53,7 +53,7 @@ __device__ __forceinline__ void record(const unsigned long long c0, const unsign
   }
 }
 
-enum Op { kFma, kAdd, kMax, kMax3, kExp, kPack, kIntXor, kFmaCvtU32, kMfmaChain, kMfma4, kMfmaF16 };
+enum Op { kFma, kAdd, kMax, kMax3, kExp, kPack, kIntXor, kFmaCvtU32, kMfmaChain, kMfma4, kMfmaF16, kMax3U32 };
 
 template <int OP>
 __global__ __launch_bounds__(256) void op_kernel(float *o, float s, const int trips) {
@@ -105,6 +105,7 @@ __global__ __launch_bounds__(256) void op_kernel(float *o, float s, const int tr
       if (OP == kPack) u[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(u[i], a[i], b[i], 0.5f, 1);
       if (OP == kIntXor) u[i] ^= u[(i + 5) & 15];
       if (OP == kFmaCvtU32) b[i] = (float)(uint32_t)fmaf(b[i], 1.0001f, 3.0f);
+      if (OP == kMax3U32) u[i] = max(max(u[i] ^ 0x5a5a5a5au, (uint32_t)i), u[(i + 1) & 15]);
     }
   }
   record(t0, w0);
@@ -332,6 +333,7 @@ int main(int argc, char **argv) {
       {op_kernel<kMfmaChain>, "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4), one chain"},
       {op_kernel<kMfma4>, "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4), 4 chains"},
       {op_kernel<kMfmaF16>, "v_mfma_f32_32x32x16_f16, 4 chains"},
+      {op_kernel<kMax3U32>, "v_xor_b32 + v_max3_u32 (one each)"},
   };
   for (const auto &op : ops) {
     double cyc, ghz;

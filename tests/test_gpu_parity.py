@@ -133,6 +133,37 @@ def test_select_ties_at_the_cutoff(frac):
     assert np.array_equal(idx.cpu().numpy(), sel_o["idx"])
 
 
+@pytest.mark.parametrize("frac,steps", [(0.2, 4), (0.2, 1000), (0.05, 1000)])
+def test_select_wide_band_at_the_cutoff(frac, steps):
+    """256 key blocks whose pooled means differ only by multiples of 2^-16 in
+    one channel: their scores differ by less than the fp32 chains' error bound,
+    so most of a long row's candidates fall in the band around the cut-off
+    (more than 64, the ranked-list size) and are ranked by their fp64 scores,
+    with exact ties (few distinct steps) or nearly none (many).  The lists must
+    equal the oracle's bit for bit."""
+    g = np.random.default_rng(11)
+    B, H, N, d = 1, 2, 64 * 256, 64
+    nb = N // 64
+    q = g.standard_normal((B, H, N, d))
+    q[..., 0] = 2.0 ** -8
+    r = g.standard_normal(d)
+    r[0] = 1.0
+    k = np.broadcast_to(r, (B, H, N, d)).copy()
+    m = g.integers(0, steps, size=(H, nb))  # block j: one row's channel 0 up by m 2^-10 (fp16-exact)
+    for h in range(H):
+        for j in range(nb):
+            k[0, h, 64 * j, 0] += m[h, j] * 2.0 ** -10
+    q16 = torch.from_numpy(q.astype(np.float16))
+    k16 = torch.from_numpy(k.astype(np.float16))
+    say(f"[case] select wide band B={B} H={H} N={N} d={d} frac={frac} steps={steps}")
+    sel_o = oracle.select(synth.bits(q16), synth.bits(k16), frac, True)
+    dev = torch.device("cuda:0")
+    idx, n16 = binding.select(q16.to(dev), k16.to(dev), frac, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(n16.cpu().numpy(), sel_o["n16"])
+    assert np.array_equal(idx.cpu().numpy(), sel_o["idx"])
+
+
 def test_output_dtypes_and_determinism():
     x = synth.generate("llama8b_16k", N=1024)
     dev = torch.device("cuda:0")
