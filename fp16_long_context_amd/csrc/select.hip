@@ -212,28 +212,33 @@ __global__ __launch_bounds__(256) void qnorm_kernel(const float *__restrict__ qb
   qn[r] = __double2float_ru(sqrt(ss));
 }
 
-// Norms of the K means ([BHkv, d, nb], channel-major source) and, per KV
-// head, their largest over blocks 1 .. nb-1 (block 0 is always on the FP16
-// list, never a candidate).  One workgroup per KV head; thread t takes
-// blocks t, t + 256, ...
+// Norms of the K means ([BHkv, d, nb], channel-major source): one thread
+// per block, so consecutive threads read consecutive blocks of a channel.
 template <int D>
 __global__ __launch_bounds__(256) void knorm_kernel(const float *__restrict__ kbarT, float *__restrict__ kn,
-                                                    float *__restrict__ knmax, const int nb) {
+                                                    const int nb, const int64_t blocks) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // = hk * nb + j
+  if (e >= blocks) return;
+  const int64_t hk = e / nb;
+  const int j = (int)(e % nb);
+  const float *kb = kbarT + hk * D * (int64_t)nb + j;
+  double ss = 0.0;
+#pragma unroll 8
+  for (int c = 0; c < D; c++) {
+    const double v = (double)kb[(int64_t)c * nb];
+    ss = fma(v, v, ss);
+  }
+  kn[e] = __double2float_ru(sqrt(ss));
+}
+
+// Per KV head, the largest K-mean norm over blocks 1 .. nb-1 (block 0 is
+// always on the FP16 list, never a candidate).  One workgroup per KV head.
+__global__ __launch_bounds__(256) void knmax_kernel(const float *__restrict__ kn, float *__restrict__ knmax,
+                                                    const int nb) {
   __shared__ float part[4];
   const int64_t hk = blockIdx.x;
-  const float *kb = kbarT + hk * D * (int64_t)nb;
   float mx = 0.0f;
-  for (int j = threadIdx.x; j < nb; j += 256) {
-    double ss = 0.0;
-#pragma unroll 8
-    for (int c = 0; c < D; c++) {
-      const double v = (double)kb[(int64_t)c * nb + j];
-      ss = fma(v, v, ss);
-    }
-    const float n = __double2float_ru(sqrt(ss));
-    kn[hk * nb + j] = n;
-    if (j > 0) mx = fmaxf(mx, n);
-  }
+  for (int j = 1 + threadIdx.x; j < nb; j += 256) mx = fmaxf(mx, kn[hk * nb + j]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mx;
@@ -652,14 +657,18 @@ __host__ __device__ constexpr size_t select_lds_per_wave(const int nb) {
 // their fp64 scores, the lower block index first among equal ones.
 template <int D, int KPL>
 __global__ __launch_bounds__(kSelThreads)
-__attribute__((amdgpu_waves_per_eu(KPL <= 16 ? 4 : (KPL <= 32 ? 3 : 1)))) void select_kernel(SelectArgs a) {
+__attribute__((amdgpu_waves_per_eu(KPL <= 16 ? 4 : (KPL <= 32 ? 3 : 1)))) void select_kernel(SelectArgs a,
+                                                                                                const int i_lo,
+                                                                                                const int i_span) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sel_lds[];
   const int nb = a.N / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kSelThreads / 64) + wave;  // = (b*Hq + h)*nb + i
-  if (row >= (int64_t)a.B * a.Hq * nb) return;
-  const int i = (int)(row % nb);
-  const int64_t bh = row / nb;
+  // this launch's rows: query blocks [i_lo, i_lo + i_span) of every (b, h)
+  const int64_t r = (int64_t)blockIdx.x * (kSelThreads / 64) + wave;
+  if (r >= (int64_t)a.B * a.Hq * i_span) return;
+  const int64_t bh = r / i_span;
+  const int i = i_lo + (int)(r % i_span);
+  const int64_t row = bh * nb + i;  // = (b*Hq + h)*nb + i
   const int nv = a.causal ? i + 1 : nb;
   const int64_t per = a.causal ? (int64_t)nb * (nb + 1) / 2 : (int64_t)nb * nb;
   int32_t *out = a.idx + bh * per + row_offset(i, nb, a.causal);
@@ -856,18 +865,31 @@ __attribute__((amdgpu_waves_per_eu(KPL <= 16 ? 4 : (KPL <= 32 ? 3 : 1)))) void s
   if (lane == 0) a.n16[row] = (int)kk;
 }
 
+// Query blocks [i_lo, i_lo + i_span) of every (b, h), with KPL keys per lane
+// (KPL >= ceil(valid blocks / 64) for every row of the range).
 template <int D, int KPL>
-static hipError_t launch_select_kpl(const SelectArgs &a, hipStream_t st) {
+static hipError_t launch_select_kpl(const SelectArgs &a, hipStream_t st, const int i_lo, const int i_span) {
   const int nb = a.N / 64;
   constexpr int waves = kSelThreads / 64;
   const size_t lds = waves * select_lds_per_wave(nb);
   const void *fn = (const void *)select_kernel<D, KPL>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int64_t rows = (int64_t)a.B * a.Hq * nb;
+  const int64_t rows = (int64_t)a.B * a.Hq * i_span;
   const unsigned grid = (unsigned)((rows + waves - 1) / waves);
-  hipLaunchKernelGGL((select_kernel<D, KPL>), dim3(grid), dim3(kSelThreads), lds, st, a);
+  hipLaunchKernelGGL((select_kernel<D, KPL>), dim3(grid), dim3(kSelThreads), lds, st, a, i_lo, i_span);
   return hipGetLastError();
+}
+
+// The rows whose valid blocks need at most KPL keys per lane: causal rows
+// [64 KPL / 2, 64 KPL) (all rows from 0 for KPL = 1) or, non-causal, every row.
+template <int D, int KPL>
+static hipError_t launch_select_class(const SelectArgs &a, hipStream_t st) {
+  const int nb = a.N / 64;
+  if (!a.causal) return launch_select_kpl<D, KPL>(a, st, 0, nb);
+  const int lo = KPL == 1 ? 0 : 64 * (KPL / 2), hi = min(nb, 64 * KPL);
+  if (lo >= hi) return hipSuccess;
+  return launch_select_kpl<D, KPL>(a, st, lo, hi - lo);
 }
 
 // The block scores of a.kind into a.idx (fp32 bits at the list positions);
@@ -930,7 +952,9 @@ static hipError_t launch_scores32_d(const SelectArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(pool_kernel<true>, dim3(grid(BHk * nb * D)), dim3(256), 0, st, a.k16, a.kbarT, BHk, a.N, D);
   hipLaunchKernelGGL(qnorm_kernel<D>, dim3((unsigned)((BHq * nb + 255) / 256)), dim3(256), 0, st, a.qbar, a.qn,
                      BHq * nb);
-  hipLaunchKernelGGL(knorm_kernel<D>, dim3((unsigned)BHk), dim3(256), 0, st, a.kbarT, a.kn, a.knmax, nb);
+  hipLaunchKernelGGL(knorm_kernel<D>, dim3((unsigned)((BHk * nb + 255) / 256)), dim3(256), 0, st, a.kbarT, a.kn, nb,
+                     BHk * nb);
+  hipLaunchKernelGGL(knmax_kernel, dim3((unsigned)BHk), dim3(256), 0, st, a.kn, a.knmax, nb);
   const int tn = (nb + kS32Tile - 1) / kS32Tile;
   const int tiles = a.causal ? tn * (tn + 1) / 2 : tn * tn;
   hipLaunchKernelGGL(score32_kernel<D>, dim3((unsigned)(BHq * tiles)), dim3(256), 0, st, a, tiles, tn);
@@ -945,14 +969,28 @@ static hipError_t launch_select_d(const SelectArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const int kpl = (nb + 63) / 64;
-  if (kpl <= 1) return launch_select_kpl<D, 1>(a, st);
-  if (kpl <= 2) return launch_select_kpl<D, 2>(a, st);
-  if (kpl <= 4) return launch_select_kpl<D, 4>(a, st);
-  if (kpl <= 8) return launch_select_kpl<D, 8>(a, st);
-  if (kpl <= 16) return launch_select_kpl<D, 16>(a, st);
-  if (kpl <= 32) return launch_select_kpl<D, 32>(a, st);
-  if (kpl <= 64) return launch_select_kpl<D, 64>(a, st);
-  return launch_select_kpl<D, 128>(a, st);
+  if (!a.causal) {
+    if (kpl <= 1) return launch_select_class<D, 1>(a, st);
+    if (kpl <= 2) return launch_select_class<D, 2>(a, st);
+    if (kpl <= 4) return launch_select_class<D, 4>(a, st);
+    if (kpl <= 8) return launch_select_class<D, 8>(a, st);
+    if (kpl <= 16) return launch_select_class<D, 16>(a, st);
+    if (kpl <= 32) return launch_select_class<D, 32>(a, st);
+    if (kpl <= 64) return launch_select_class<D, 64>(a, st);
+    return launch_select_class<D, 128>(a, st);
+  }
+  // causal: row i has i + 1 valid blocks, so each power-of-two class of
+  // rows gets the smallest KPL that holds them (the short rows do not pay
+  // for the longest row's key slots)
+  hipError_t e;
+  if ((e = launch_select_class<D, 1>(a, st)) != hipSuccess) return e;
+  if ((e = launch_select_class<D, 2>(a, st)) != hipSuccess) return e;
+  if ((e = launch_select_class<D, 4>(a, st)) != hipSuccess) return e;
+  if ((e = launch_select_class<D, 8>(a, st)) != hipSuccess) return e;
+  if ((e = launch_select_class<D, 16>(a, st)) != hipSuccess) return e;
+  if ((e = launch_select_class<D, 32>(a, st)) != hipSuccess) return e;
+  if ((e = launch_select_class<D, 64>(a, st)) != hipSuccess) return e;
+  return launch_select_class<D, 128>(a, st);
 }
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t st) {
