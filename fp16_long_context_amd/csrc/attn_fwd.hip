@@ -19,9 +19,9 @@
 //     wave owns 32 query rows of one head and computes the blocks on its own
 //     head's FP4 list; the others are skipped.  It normalises and stores the
 //     rows, unless the overflow rule below flags the workgroup.
-//   * attn_redo_kernel: exits at once unless its work item was flagged, and
-//     then recomputes it from scratch with the general walk (every block in
-//     ascending order, FP16 or FP4 per head, M raised by either kind).
+//   * attn_redo_kernel: a small grid that reads every work item's flag and
+//     recomputes the flagged ones from scratch with the general walk (every
+//     block in ascending order, FP16 or FP4 per head, M raised by either kind).
 // Every tile is S^T = K Q^T with 32x32 MFMAs (FP16: v_mfma_f32_32x32x16_f16;
 // FP4: v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 scales), then
 // O^T += V^T P^T.
@@ -597,13 +597,14 @@ __device__ __forceinline__ void tile_fp16(const uint8_t *st16, const uint8_t *qr
 // chunk).
 struct WorkItem {
   int i, b, g, h0, nh, nb, group, nv, nw;
-  __device__ __forceinline__ WorkItem(const AttnArgs &a, const int hpw) {
+  // item: the work item's index in its launch (the FP4 kernel's workgroup)
+  __device__ __forceinline__ WorkItem(const AttnArgs &a, const int hpw, const int item) {
     nb = a.N / 64;
     group = a.Hq / a.Hkv;
     const int chunks = (a.hspan + hpw - 1) / hpw;
     const int per_i = a.B * a.Hkv * chunks;
-    const int wi = blockIdx.x / per_i;
-    int rem = blockIdx.x % per_i;
+    const int wi = item / per_i;
+    int rem = item % per_i;
     i = a.causal ? nb - 1 - wi : wi;
     b = rem / (a.Hkv * chunks);
     rem %= a.Hkv * chunks;
@@ -1077,13 +1078,12 @@ __device__ __forceinline__ int *redo_flags(const AttnArgs &a) {
 // (block j in slots j % 2), with tile bodies that raise M whenever a block
 // needs it; then the rows are stored.  Same grid as the FP4 kernel; a
 // workgroup whose item was not flagged returns at once.
+// One flagged work item of the redo walk (smem: the workgroup's LDS).
 template <int D, int HPW, int R>
-__global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
+__device__ __forceinline__ void redo_item(const AttnArgs &a, const int item, uint8_t *smem) {
   using T = Tile<D, HPW>;
   constexpr int KS4 = D / 64, CB = D / 32;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  if (redo_flags(a)[blockIdx.x] == 0) return;
-  const WorkItem w(a, HPW);
+  const WorkItem w(a, HPW, item);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = wave_u >> 1, qhalf = wave_u & 1;
@@ -1157,12 +1157,31 @@ __global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a) {
   if (head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
 }
 
+// The redo walk over the FP4 launch's `items` work items: workgroup w takes
+// the run of `per` items from w * per (per <= its thread count), reads their
+// flags at once (one per thread) and, in the common case that none is set,
+// exits after one barrier; otherwise it redoes the flagged ones in turn.  A
+// small grid keeps the common case to a few microseconds.
+template <int D, int HPW, int R>
+__global__ __launch_bounds__(128 * HPW) void attn_redo_kernel(AttnArgs a, const int items, const int per) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int first = (int)blockIdx.x * per;
+  const int n = min(per, items - first);
+  const int f = ((int)threadIdx.x < n) ? redo_flags(a)[first + threadIdx.x] : 0;
+  if (!__syncthreads_or(f)) return;
+  for (int k = 0; k < n; k++) {
+    if (redo_flags(a)[first + k] == 0) continue;  // the same value for every thread
+    redo_item<D, HPW, R>(a, first + k, smem);
+    __syncthreads();  // the next item rewrites the masks and tiles in LDS
+  }
+}
+
 // ---------------------------------------------------------------------------
 // FP4 kernel: one workgroup per query block i of HPW heads of a GQA group
 // (a wave owns 32 rows of one head).  Each wave starts from the partial state
 // its head's FP16 blocks left in the workspace and walks, ascending, every
 // block below the diagonal that some head of the workgroup has on its FP4
-// list, with the FP4 QK product one block ahead.  The walk is the same for
+// list, the next block's K/V tiles loading during each step.  The walk is the same for
 // all waves (K/V tiles are shared in LDS); a head skips a block of its own
 // FP16 list by adding neither p to l nor P.V to the accumulator.
 template <int D, int HPW, int R>
@@ -1177,7 +1196,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   uint32_t *mask = (uint32_t *)(smem + T::f4MASK);  // [HPW][kMaxBlocks/32] FP16-list bits
   uint32_t *imask = (uint32_t *)(smem + T::f4IMASK);  // blocks on every head's FP16 list
 
-  const WorkItem w(a, HPW);
+  const WorkItem w(a, HPW, (int)blockIdx.x);
   const int i = w.i, b = w.b, g = w.g, nb = w.nb, group = w.group, nv = w.nv, nw = w.nw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1347,6 +1366,21 @@ __global__ __launch_bounds__(128 * HPW) void attn_fwd_kernel(AttnArgs a) {
   if (!flagged && head_ok) store_rows<D>(a, acc, M, l_part, qrow, lh);
 }
 
+// Redo launch over `items` FP4 work items with `threads` per workgroup:
+// about kRedoGrid workgroups, each a run of at most `threads` items.
+constexpr unsigned kRedoGrid = 2048;
+struct RedoGrid {
+  unsigned grid;
+  int per;
+  RedoGrid(const unsigned items, const unsigned threads) {
+    unsigned g = items < kRedoGrid ? items : kRedoGrid;
+    const unsigned need = (items + threads - 1) / threads;  // runs no longer than a workgroup
+    g = g > need ? g : need;
+    per = (int)((items + g - 1) / g);
+    grid = (items + (unsigned)per - 1) / (unsigned)per;  // every workgroup has at least one item
+  }
+};
+
 template <int D, int HPW, int R>
 static hipError_t set_fp4_attrs() {
   using T = Tile<D, HPW>;
@@ -1397,11 +1431,15 @@ static hipError_t launch_d(const AttnArgs &a, hipStream_t st, hipEvent_t const *
   }
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   if (pairs) {
-    hipLaunchKernelGGL((attn_redo_kernel<D, 2, R>), grid2, dim3(256), (Tile<D, 2>::LDS), st, a2);
+    const RedoGrid r2(grid2.x, 256);
+    hipLaunchKernelGGL((attn_redo_kernel<D, 2, R>), dim3(r2.grid), dim3(256), (Tile<D, 2>::LDS), st, a2,
+                       (int)grid2.x, r2.per);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (single) {
-    hipLaunchKernelGGL((attn_redo_kernel<D, 1, R>), grid1, dim3(128), (Tile<D, 1>::LDS), st, a1);
+    const RedoGrid r1(grid1.x, 128);
+    hipLaunchKernelGGL((attn_redo_kernel<D, 1, R>), dim3(r1.grid), dim3(128), (Tile<D, 1>::LDS), st, a1,
+                       (int)grid1.x, r1.per);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (ev) e = hipEventRecord(ev[3], st);
