@@ -1,9 +1,9 @@
 """Quality studies of the mixed FP16/FP4 attention on seeded synthetic inputs.
 
 The method's claim ("ThriftAttention: Selective Mixed Precision for
-Long-Context FP4 Attention", abstract) is that computing a small share of
-query-key blocks in FP16 recovers most of the FP4-to-FP16 quality gap, and
-that the benefit grows with sequence length.  The pages measure this on
+Long-Context FP4 Attention", abstract) is that a small FP16 share of the
+block pairs recovers most of the quality lost by going from FP16 to FP4,
+and that this pays off more as sequences get longer.  The pages measure this on
 benchmarks with trained models; here the planted-needle workloads stand in:
 
 * errors(): err(f) = ||O_f - O_1||_F / ||O_1||_F against the all-FP16 output

@@ -2,10 +2,10 @@
  * thrift.h -- C ABI of the MI355X (gfx950) ThriftAttention prefill library.
  *
  * The method ("ThriftAttention: Selective Mixed Precision for Long-Context
- * FP4 Attention", abstract): a heuristic first picks a small number of
- * important query-key block pairs for FP16; the picked blocks are then
- * computed in FP16 and all other causally valid blocks in block-scaled
- * 4-bit, and both paths are merged by online softmax into one output.  The
+ * FP4 Attention", abstract): a cheap heuristic first marks the few
+ * query-key block pairs that matter most; those run at FP16 precision and
+ * every other causally valid block in block-scaled 4-bit, and one online
+ * softmax combines the two kinds of block into the result.  The
  * three calls below are the three steps of that path:
  *
  *   thrift_quantize   FP16 copies of Q/K/V and their MXFP4 codes

@@ -6,9 +6,9 @@ never imports this package and this package never imports the product.
 
 The arithmetic lives in oracle.c (plain fp64 C, OpenMP over rows); this file
 only marshals numpy arrays.  Every function follows a step of the method as
-the ThriftAttention abstract states it (heuristic selection of important
-query-key block pairs, FP16 for those, block-scaled 4-bit for the rest,
-online-softmax merge), with the readings listed at the top of oracle.c.
+the ThriftAttention abstract states it (a heuristic marks the block pairs
+that matter, FP16 for those, block-scaled 4-bit for the rest, one online
+softmax over both), with the readings listed at the top of oracle.c.
 
 Parity status per function:
   to_fp16, mx_encode, quantize  pinned (numpy float16 cast, brute-force E2M1

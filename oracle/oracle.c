@@ -8,11 +8,11 @@
  *
  * What it follows ("ThriftAttention: Selective Mixed Precision for
  * Long-Context FP4 Attention", abstract):
- *   - stage 1: a heuristic picks a small number of important query-key block
- *     pairs for FP16;
- *   - stage 2: the picked blocks are computed in FP16, every other block in
- *     block-scaled 4-bit, and both paths are merged by online softmax into one
- *     output.
+ *   - stage 1: a cheap heuristic marks the few query-key block pairs that
+ *     matter most;
+ *   - stage 2: those run at FP16 precision, every other block in
+ *     block-scaled 4-bit, and one online softmax combines the two kinds of
+ *     block into the result.
  * The abstract leaves the heuristic, the 4-bit format, the block size, the
  * budget rule and the handling of P open.  The readings used here are:
  *   - 4-bit format: OCP MXFP4 (E2M1 elements, one E8M0 scale per 32
