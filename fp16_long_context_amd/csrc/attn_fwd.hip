@@ -343,6 +343,16 @@ struct Fp4Offsets {
     // swz_v4 of channel 32 cb + col depends on col only
     v = vb + T::oV4 + col * 32 + 16 * (lh ^ swz_v4(col));
     vs = vb + T::oV4S + col * 2 + lh;
+    // opaque to the compiler, so that the walk keeps these addresses in
+    // registers instead of re-deriving them with adds at every step
+#pragma unroll
+    for (int blk = 0; blk < 2; blk++) {
+#pragma unroll
+      for (int kk = 0; kk < D / 64; kk++) asm volatile("" : "+v"(k[blk][kk]));
+      asm volatile("" : "+v"(ks[blk]));
+    }
+    asm volatile("" : "+v"(v));
+    asm volatile("" : "+v"(vs));
   }
 };
 
