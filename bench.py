@@ -67,7 +67,7 @@ PEAK_HBM = 8000.0  # GB/s, MI355X HBM3E
 VALU_CYCLES = {"v_fma_f32": 2.83, "v_exp_f32": 9.99, "v_add_f32": 2.83, "v_cvt_scalef32_pk_fp4_f32": 8.42,
                "v_max3_f32": 4.72, "v_max_f32": 5.73, "integer": 2.87}
 FP4_BLOCK_VALU = {"v_fma_f32": 32, "v_exp_f32": 32, "v_add_f32": 32, "v_cvt_scalef32_pk_fp4_f32": 16,
-                  "v_max3_f32": 14, "v_max_f32": 3, "integer": 11}
+                  "v_max3_f32": 14, "v_max_f32": 3, "integer": 6}
 FP4_BLOCK_MFMAS = 8  # 4 for S, 4 for P.V, v_mfma_scale_f32_32x32x64_f8f6f4
 MFMA_F4_CYCLES = 32.0  # 2 x 32 x 32 x 64 flops at the dense MXFP4 peak per SIMD (10066 TF/s / 1024 / 2.4 GHz)
 SIMDS, NOMINAL_GHZ = 1024, 2.4
