@@ -11,8 +11,8 @@ Prints one JSON line:
   roofline   the fused attention call thrift_attn_fwd, which is three
              launches on one stream (attn_f16_kernel: FP16 blocks per head;
              attn_fwd_kernel: FP4 blocks per GQA group, finishing each row;
-             attn_redo_kernel: exits at once unless an FP4 workgroup flagged
-             an overflow): achieved = F / the call's average duration (HIP
+             attn_redo_kernel: reads the FP4 workgroups' overflow flags and
+             redoes the flagged ones): achieved = F / the call's average duration (HIP
              events on its stream), peak = the FP16/MXFP4 MFMA roofline
              weighted by the flops in FP16 and FP4 tiles
              (F16 / 2516.6 TF/s + F4 / 10066 TF/s), traffic = HBM bytes per
@@ -277,10 +277,21 @@ def time_workload(torch, binding, synth, name, fracs, dev, steps=4, warmup=2):
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it (model name, family/model
+    numbers, clock and cache of the first CPU), else the platform's name."""
     try:
+        info = {}
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if not line.strip():
+                break  # the first CPU's fields only
+            k, _, v = line.partition(":")
+            info.setdefault(k.strip(), v.strip())
+        if "model name" in info:
+            extra = [f"family {info[k1]} model {info[k2]}" for k1, k2 in [("cpu family", "model")]
+                     if k1 in info and k2 in info]
+            extra += [f"{info[k]} MHz" for k in ["cpu MHz"] if k in info]
+            extra += [f"cache {info[k]}" for k in ["cache size"] if k in info]
+            return info["model name"] + (f" ({', '.join(extra)})" if extra else "")
     except OSError:
         pass
     import platform
