@@ -20,8 +20,10 @@ Parity status per function:
                                 dominant key row for max-pooled; equal-norm rows
                                 reduce norm-weighted to the pooled mean)
   attn_rows                     pinned (frac=1 against textbook softmax
-                                attention, FP4-exact inputs against textbook
-                                attention, closed forms, split-merge);
+                                attention, frac=0 against an independent
+                                numpy pure-FP4 attention on random inputs,
+                                FP4-exact inputs against textbook attention,
+                                closed forms, split-merge);
                                 rowsum="weights": V = 1 gives O = 1 exactly,
                                 frac=1 against textbook attention, split-merge,
                                 closed forms; rowsum="log": the same, plus
