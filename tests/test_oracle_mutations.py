@@ -42,6 +42,10 @@ MISTAKES = [
     ("exp-free codes: stand-in without the leading 1", "z = ldexp(1.0 + (y - f), (int)f);", "z = ldexp(y - f, (int)f);"),
     ("exp-free codes: group exponent off by one", "(int)floor(xmax - M) - 2;", "(int)floor(xmax - M) - 1;"),
     ("exp-free reading falls back to exact codes", "if (rowsum == 2) {", "if (rowsum == 3) {"),
+    ("pooled mean over 63 rows", "out[(bh * nb + i) * d + c] = (float)(s / 64.0);",
+     "out[(bh * nb + i) * d + c] = (float)(s / 63.0);"),
+    ("LSE left in log2 units", "(M + log2(l)) * 0.69314718055994530942", "(M + log2(l))"),
+    ("score scale without log2(e)", "(double)sm * 1.4426950408889634074", "(double)sm"),
 ]
 CONTROL = ("control: no change in meaning", "l += p[key];", "l += 1.0 * p[key];")
 
