@@ -4,8 +4,10 @@ and an edit that changes nothing (the control) must leave it passing.
 
 CPU only.  Every mistake runs the pins in a subprocess on its own copy (the
 oracle package builds its library next to its source), stopping at the first
-failing pin.
+failing pin; the copies run side by side, a few at a time, and each test
+then reads its mistake's outcome.
 """
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -50,7 +52,7 @@ MISTAKES = [
 CONTROL = ("control: no change in meaning", "l += p[key];", "l += 1.0 * p[key];")
 
 
-def _run_pins(tmp_path, old, new):
+def _run_pins(tmp_path, old, new, threads):
     work = tmp_path / "copy"
     work.mkdir()
     shutil.copytree(os.path.join(ROOT, "oracle"), work / "oracle",
@@ -64,20 +66,33 @@ def _run_pins(tmp_path, old, new):
     src = src_path.read_text()
     assert src.count(old) >= 1, f"text not found in oracle.c: {old}"
     src_path.write_text(src.replace(old, new))
-    env = dict(os.environ, OMP_NUM_THREADS=os.environ.get("OMP_NUM_THREADS", "4"))
+    env = dict(os.environ, OMP_NUM_THREADS=str(threads))
     r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-x", "-q", "-p", "no:cacheprovider"],
                        cwd=work, capture_output=True, text=True, timeout=900, env=env)
     return r.returncode, (r.stdout + r.stderr)[-800:]
 
 
+@pytest.fixture(scope="module")
+def outcomes(tmp_path_factory):
+    """(return code, output tail) of the pins on every mistake and the
+    control, keyed by description."""
+    cases = list(MISTAKES) + [CONTROL]
+    workers = max(1, min(len(cases), (os.cpu_count() or 2) // 2))
+    threads = max(1, (os.cpu_count() or 2) // workers)
+    dirs = [tmp_path_factory.mktemp(f"mistake{i}") for i in range(len(cases))]
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        runs = ex.map(lambda a: (a[1][0], _run_pins(a[0], a[1][1], a[1][2], threads)), zip(dirs, cases))
+        return dict(runs)
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("what,old,new", MISTAKES, ids=[m[0] for m in MISTAKES])
-def test_pins_catch_planted_mistake(tmp_path, what, old, new):
-    rc, tail = _run_pins(tmp_path, old, new)
+@pytest.mark.parametrize("what", [m[0] for m in MISTAKES])
+def test_pins_catch_planted_mistake(outcomes, what):
+    rc, tail = outcomes[what]
     assert rc == 1, f"{what}: the pins did not fail (rc {rc})\n{tail}"
 
 
 @pytest.mark.slow
-def test_control_edit_passes(tmp_path):
-    rc, tail = _run_pins(tmp_path, CONTROL[1], CONTROL[2])
+def test_control_edit_passes(outcomes):
+    rc, tail = outcomes[CONTROL[0]]
     assert rc == 0, f"control edit broke the pins (rc {rc})\n{tail}"
