@@ -1007,7 +1007,9 @@ hipError_t launch_block_scores(const SelectArgs &a, hipStream_t st) {
 // Host code never passes the array's name to a kernel (in host code it is a
 // stand-in, not a device address): the first call on each device looks up
 // the array's device address with hipGetSymbolAddress, with that device
-// current, and every call uses that pointer.  Calls on one GPU share the
+// current, and every call uses that pointer.  The device is the stream's
+// (the current device for the default stream), so a stream of another GPU
+// than the current one gets that GPU's copy.  Calls on one GPU share the
 // array, so calls that overlap in time on one GPU race; each call rewrites
 // every pooled mean it reads, so nothing needs clearing between calls.
 static __device__ __align__(256) uint8_t scratch[kSelectScratchBytes];
@@ -1020,16 +1022,21 @@ void *g_scratch_ptr[kMaxDevices];
 
 hipError_t launch_select_scratch(SelectArgs a, hipStream_t st) {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   void *ptr;
   {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
+      int cur = 0;
+      if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
       void *p = nullptr;
       e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;  // the caller's device again
       if (e != hipSuccess) return e;
+      if (back != hipSuccess) return back;
       if (!p) return hipErrorInvalidSymbol;
       g_scratch_ptr[dev] = p;
     }

@@ -184,7 +184,8 @@ int thrift_block_scores(const thrift_shape *s, int score, const void *q16, const
  * until the process ends); the call itself allocates nothing.  Limit:
  * thrift_select_workspace_bytes(s) must not exceed 64 MiB (e.g. B = 1,
  * Hq = 32, Hkv = 8, d = 128 up to N = 208064),
- * else THRIFT_EWORKSPACE and nothing is launched.  Every call on one GPU
+ * else THRIFT_EWORKSPACE and nothing is launched.  The GPU is the stream's
+ * (the current device for the default stream).  Every call on one GPU
  * shares that array: calls that overlap in time on one GPU (other streams,
  * other threads) race and must be serialized by the caller.
  * Errors: those of thrift_select, THRIFT_EWORKSPACE beyond the limit.
