@@ -27,6 +27,23 @@ int check_shape(const thrift_shape *s) {
 
 bool aligned_ok(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 
+// Runs launch() with the stream's GPU current (HIP applies the kernels'
+// shared-memory attributes and symbol lookups to the current device), then
+// makes the caller's device current again.  The default stream (NULL) runs
+// on the current device.
+template <class F>
+int on_stream_device(void *stream, F launch) {
+  int cur = 0, dev = 0;
+  if (stream) {
+    if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess || hipGetDevice(&cur) != hipSuccess)
+      return THRIFT_EHIP;
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return THRIFT_EHIP;
+  }
+  const hipError_t e = launch();
+  if (stream && dev != cur && hipSetDevice(cur) != hipSuccess) return THRIFT_EHIP;
+  return e == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,7 +86,7 @@ int thrift_quantize(const thrift_shape *s, int in_dtype, const void *q, const vo
   a.v4 = (uint8_t *)v4; a.v4s = (uint8_t *)v4s;
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d;
   a.bf16 = in_dtype == THRIFT_BF16;
-  return launch_quantize(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+  return on_stream_device(stream, [&] { return launch_quantize(a, (hipStream_t)stream); });
 }
 
 int thrift_select(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx, int32_t *n16,
@@ -89,7 +106,7 @@ int thrift_select(const thrift_shape *s, double frac, const void *q16, const voi
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
   select_layout(a, (float *)workspace);
   a.ppm = (int64_t)llround(frac * 1e6);
-  return launch_select(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+  return on_stream_device(stream, [&] { return launch_select(a, (hipStream_t)stream); });
 }
 
 static int select_args(const thrift_shape *s, double frac, int score, const void *q16, const void *k16,
@@ -118,7 +135,7 @@ int thrift_select_ex(const thrift_shape *s, double frac, int score, const void *
   SelectArgs a;
   const int rc = select_args(s, frac, score, q16, k16, idx, n16, workspace, ws_bytes, a);
   if (rc != THRIFT_OK) return rc;
-  return launch_select(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+  return on_stream_device(stream, [&] { return launch_select(a, (hipStream_t)stream); });
 }
 
 int thrift_block_scores(const thrift_shape *s, int score, const void *q16, const void *k16, float *scores,
@@ -127,7 +144,7 @@ int thrift_block_scores(const thrift_shape *s, int score, const void *q16, const
   // n16 is not written: any aligned non-null pointer passes validation
   const int rc = select_args(s, 1.0, score, q16, k16, (int32_t *)scores, (int32_t *)scores, workspace, ws_bytes, a);
   if (rc != THRIFT_OK) return rc;
-  return launch_block_scores(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+  return on_stream_device(stream, [&] { return launch_block_scores(a, (hipStream_t)stream); });
 }
 
 int thrift_select_noalloc(const thrift_shape *s, double frac, const void *q16, const void *k16, int32_t *idx,
@@ -146,7 +163,7 @@ int thrift_select_noalloc(const thrift_shape *s, double frac, const void *q16, c
   a.qbar = a.kbarT = a.qn = a.kn = a.knmax = nullptr;  // set by the launcher
   a.B = s->B; a.Hq = s->Hq; a.Hkv = s->Hkv; a.N = s->N; a.d = s->d; a.causal = s->causal;
   a.ppm = (int64_t)llround(frac * 1e6);
-  return launch_select_scratch(a, (hipStream_t)stream) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+  return on_stream_device(stream, [&] { return launch_select_scratch(a, (hipStream_t)stream); });
 }
 
 size_t thrift_attn_workspace_bytes(const thrift_shape *s) {
@@ -180,7 +197,7 @@ static int attn_fwd_common(const thrift_shape *s, float sm_scale, const void *q1
   // score scale in log2 units, rounded once to fp32
   const float sm = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)s->d));
   a.c = (float)((double)sm * 1.4426950408889634074);
-  return launch_attn_fwd(a, (hipStream_t)stream, (hipEvent_t const *)events) == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+  return on_stream_device(stream, [&] { return launch_attn_fwd(a, (hipStream_t)stream, (hipEvent_t const *)events); });
 }
 
 int thrift_attn_fwd(const thrift_shape *s, float sm_scale, const void *q16, const void *k16, const void *v16,

@@ -18,7 +18,9 @@
  *   - Tensor pointers are DEVICE pointers owned and allocated by the caller;
  *     the library allocates nothing, keeps no state between calls and never
  *     synchronizes.  All work is enqueued on `stream` (a hipStream_t; NULL =
- *     the default stream) and is asynchronous; calls are reentrant.
+ *     the default stream) and is asynchronous; calls are reentrant.  A call
+ *     makes the stream's GPU current while it launches and the caller's
+ *     device current again before it returns.
  *   - Every pointer must be 16-byte aligned.
  *   - Return value: THRIFT_OK (0) or a negative thrift_status.  Arguments are
  *     validated on the host before anything is enqueued, so an error return
