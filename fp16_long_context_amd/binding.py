@@ -96,6 +96,8 @@ def _need_gpu(*ts):
     for t in ts:
         if not (t.is_cuda and t.is_contiguous()):
             raise ThriftError("tensors must be contiguous and on a GPU")
+        if t.device != ts[0].device:
+            raise ThriftError(f"tensors must all be on one GPU ({ts[0].device} and {t.device})")
 
 
 def alloc_quantized(B, Hq, Hkv, N, d, device) -> dict:

@@ -192,6 +192,24 @@ def test_binding_refuses_cpu_tensors():
         binding.quantize(q, q, q)
 
 
+def test_binding_refuses_tensors_on_two_gpus():
+    # stand-ins with the attributes the device check reads (no GPU here)
+    import torch
+
+    class Dev:
+        is_cuda = True
+
+        def __init__(self, d):
+            self.device = torch.device(d)
+
+        def is_contiguous(self):
+            return True
+
+    binding._need_gpu(Dev("cuda:0"), Dev("cuda:0"))
+    with pytest.raises(binding.ThriftError, match="one GPU"):
+        binding._need_gpu(Dev("cuda:0"), Dev("cuda:0"), Dev("cuda:1"))
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     # no fallback: a missing library is an error, not a silent CPU path
     monkeypatch.setattr(binding, "_lib", None)
