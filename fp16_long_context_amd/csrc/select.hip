@@ -859,7 +859,11 @@ __attribute__((amdgpu_waves_per_eu(KPL <= 16 ? 4 : (KPL <= 32 ? 3 : 1)))) void s
     }
     const uint64_t sb = __ballot(valid && sel);
     const int p16 = before16 + __popcll(sb & lower);
-    if (valid) out[sel ? p16 : (int)kk + (j - p16)] = j;
+    // finite scores select exactly kk blocks, so every position is below
+    // nv; non-finite inputs (outside the contract) may select fewer, and
+    // their positions past the row are dropped rather than written
+    const int pos = sel ? p16 : (int)kk + (j - p16);
+    if (valid && pos < nv) out[pos] = j;
     before16 += __popcll(sb);
   }
   if (lane == 0) a.n16[row] = (int)kk;

@@ -278,6 +278,43 @@ def test_attention_composer_and_sm_scale():
     assert err <= TOL
 
 
+def test_non_finite_inputs_stay_in_bounds():
+    """Inputs outside the contract (inf and NaN) give undefined lists and
+    outputs, but every write stays inside its buffer: the slack after idx
+    keeps its fill, every list entry is a block of its row or the fill, and
+    the attention call completes."""
+    g = np.random.default_rng(3)
+    B, Hq, Hkv, N, d = 1, 2, 1, 1024, 64
+    q, k, v = g.standard_normal((B, Hq, N, d)), g.standard_normal((B, Hkv, N, d)), g.standard_normal((B, Hkv, N, d))
+    q[0, 0, 5, 3] = np.nan
+    q[0, 1, 900, 2] = np.inf
+    k[0, 0, 70, 1] = np.inf
+    k[0, 0, 200, 0] = -np.inf
+    v[0, 0, 300, 7] = np.nan
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.from_numpy(x.astype(np.float16)).to(dev)
+    say(f"[case] non-finite inputs B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}")
+    qz = binding.quantize(t(q), t(k), t(v))
+    nb = N // 64
+    ents = B * Hq * nb * (nb + 1) // 2
+    fill = -7
+    idx = torch.full((ents + 4096,), fill, dtype=torch.int32, device=dev)
+    n16 = torch.full((B, Hq, nb), fill, dtype=torch.int32, device=dev)
+    row_of = np.tile(np.repeat(np.arange(nb), np.arange(1, nb + 1)), B * Hq)  # query block of each entry
+    for frac in (0.05, 0.3, 1.0):
+        idx.fill_(fill)
+        binding.select(qz["q16"], qz["k16"], frac, True, idx=idx, n16=n16)
+        out, lse = binding.attn_fwd(qz, idx, n16, True, want_lse=True)
+        torch.cuda.synchronize()
+        i = idx.cpu().numpy()
+        assert np.all(i[ents:] == fill), f"frac {frac}: a list write left the array"
+        e = i[:ents]
+        assert np.all((e == fill) | ((e >= 0) & (e <= row_of))), f"frac {frac}: an entry outside its row"
+        c = n16.cpu().numpy().reshape(B * Hq, nb)
+        assert np.all((c >= 1) & (c <= np.arange(1, nb + 1))), f"frac {frac}: a count outside its row"
+        assert out.shape == (B, Hq, N, d) and lse.shape == (B, Hq, N)
+
+
 def test_maximum_blocks():
     # N = 64 * 8192, the largest supported block count
     q, k, v = synth.random_qkv(1, 2, 1, 64 * 8192, 64, "fp16", seed=77)
