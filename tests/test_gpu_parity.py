@@ -186,6 +186,39 @@ def test_output_dtypes_and_determinism():
     assert torch.equal(o2, o32)
 
 
+def test_preallocated_buffers_are_fully_written():
+    """Every output is written completely: caller buffers filled with garbage
+    and reused for two different problems give the bits of fresh buffers."""
+    dev = torch.device("cuda:0")
+    xs = [synth.generate("llama8b_16k", N=1024), synth.generate("long_128k", N=1024)]
+    B, Hq, N, d = xs[0]["q"].shape
+    Hkv = xs[0]["k"].shape[1]
+    say(f"[case] preallocated buffers B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}")
+    qb = binding.alloc_quantized(B, Hq, Hkv, N, d, dev)
+    for t in qb.values():
+        t.view(torch.uint8).fill_(0x7F)
+    ents = binding.list_entries(B, Hq, N)
+    idx = torch.full((ents,), 12345, dtype=torch.int32, device=dev)
+    n16 = torch.full((B, Hq, N // 64), 777, dtype=torch.int32, device=dev)
+    sws = torch.full((1 << 22,), 0xAB, dtype=torch.uint8, device=dev)
+    out = torch.full((B, Hq, N, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=dev)
+    aws = torch.full((binding.attn_workspace_bytes(B, Hq, Hkv, N, d),), 0xCD, dtype=torch.uint8, device=dev)
+    for x in xs:
+        q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+        fq = binding.quantize(q, k, v)
+        fi, fn = binding.select(fq["q16"], fq["k16"], 0.05)
+        fo, fl = binding.attn_fwd(fq, fi, fn, want_lse=True)
+        rq = binding.quantize(q, k, v, out=qb)
+        binding.select(rq["q16"], rq["k16"], 0.05, idx=idx, n16=n16, workspace=sws)
+        binding.attn_fwd(rq, idx, n16, want_lse=True, out=out, lse=lse, workspace=aws)
+        torch.cuda.synchronize()
+        for n in fq:
+            assert torch.equal(rq[n].view(torch.uint8), fq[n].view(torch.uint8)), n
+        assert torch.equal(idx, fi) and torch.equal(n16, fn)
+        assert torch.equal(out, fo) and torch.equal(lse, fl)
+
+
 def sample_rows(x, B, Hq, N, n, seed, heads=(), batches=None):
     """Rows to compare at full size: n random rows, the last row of the first
     and last head of every batch, rows that look up a planted needle, and
