@@ -219,6 +219,54 @@ def test_preallocated_buffers_are_fully_written():
         assert torch.equal(out, fo) and torch.equal(lse, fl)
 
 
+def test_graph_capture_replays_match_eager():
+    """The three calls on caller buffers can be captured in a HIP graph (they
+    allocate nothing and record no memset): three replays, with eager work and
+    synchronizations between them, each equal the eager run bit for bit."""
+    dev = torch.device("cuda:0")
+    x = synth.generate("llama8b_16k", N=1024)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    say(f"[case] graph capture B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}")
+    qb = binding.alloc_quantized(B, Hq, Hkv, N, d, dev)
+    idx = torch.empty(binding.list_entries(B, Hq, N), dtype=torch.int32, device=dev)
+    n16 = torch.empty((B, Hq, N // 64), dtype=torch.int32, device=dev)
+    sws = torch.empty(1 << 22, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    aws = torch.empty(binding.attn_workspace_bytes(B, Hq, Hkv, N, d), dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.quantize(q, k, v, out=qb)
+        binding.select(qb["q16"], qb["k16"], 0.05, idx=idx, n16=n16, workspace=sws)
+        binding.attn_fwd(qb, idx, n16, want_lse=True, out=out, lse=lse, workspace=aws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in qb.items()}
+    ref_idx, ref_n16, ref_out, ref_lse = idx.clone(), n16.clone(), out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        for t in (idx, n16):  # eager work between replays: stale values in every output
+            t.fill_(-3)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in ref:
+            assert torch.equal(qb[n].view(torch.uint8), ref[n].view(torch.uint8)), (r, n)
+        assert torch.equal(idx, ref_idx) and torch.equal(n16, ref_n16), r
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), r
+
+
 def sample_rows(x, B, Hq, N, n, seed, heads=(), batches=None):
     """Rows to compare at full size: n random rows, the last row of the first
     and last head of every batch, rows that look up a planted needle, and
